@@ -1,0 +1,362 @@
+"""Plain float64 reference of GPTQ layer-wise weight quantization (test infrastructure only).
+
+Sources (cited by page title and section):
+  [Q]   page "量化" (Quantization), dingiv.github.io/ai/compute/kernel/quantization
+        - section "量化基础" (quantization basics): symmetric form x_q = round(x/s),
+          asymmetric form x_q = round(x/s + z), rounding and clipping errors;
+        - section "GPTQ": layer objective argmin ||WX - W^X||^2, Hessian H = 2XX^T,
+          OBS compensation formula, fixed left-to-right order, Cholesky of H^-1,
+          blocks of B = 128 columns with a lazy batch update, per-channel output.
+  [G]   page "大模型常见的量化方式" (psvmc.cn), section "按量化粒度划分" (granularity
+        table): per-channel and group-wise (128 elements per group) quantization.
+  [L]   page on LLM quantization (m.youleyou.com), section "二、量化是什么" (the
+        [-T, T] -> [-127, 127] mapping) and section "四、量化形式" (linear
+        quantization with round() and clip() to [qmin, qmax], scale s, offset z).
+
+Readings where the pages are silent or garbled (each function names the one it uses):
+  R1  the garbled norm of the objective is the squared Frobenius norm over rows.
+  R2  the OBS formula uses the inverse Hessian of the not-yet-quantized set; row q
+      of G = Cholesky(H^-1)^T (upper), scaled by G_qq, is that column.
+  R3  "Cholesky(H^-1)^T" is the transposed lower Cholesky factor: upper, GᵀG = H^-1.
+  R4  natural column order 0..d_col-1, no reordering.
+  R5  damping (not on the pages): H_d = H + lambda I, lambda = frac * mean(diag H).
+  R6  H is literally 2 X X^T (not averaged).
+  R7  group (s, z) are set at the group's first column from the current values.
+  R8  symmetric: s = max|x| / (2^(b-1) - 1), signed codes clipped to
+      [-2^(b-1), 2^(b-1) - 1], stored with offset z = 2^(b-1).
+      asymmetric: range [min(0, min x), max(0, max x)], s = range / (2^b - 1),
+      z = round(-xmin / s); degenerate range -> [-1, 1].
+  R9  code = clip(round(x/s + z), 0, 2^b - 1), round half to even.
+  R13 groups are runs of g consecutive input columns of one row.
+  P1  every decision that turns a float into an integer (z and the codes) is taken
+      in float32, the precision of the GPU kernels; the state (current weights,
+      H, G, errors) stays float64.
+
+Pins (tests/test_oracle_pins.py): hand-solved 1x2 and 2x3 layers (tests/golden),
+brute-force Hessian, G^T G H_d = I and agreement of two independent G routes,
+the literal OBS formula with explicit inverses, the conditional least-squares
+re-fit, H proportional to I giving round-to-nearest exactly, the identity
+sum(e^2) = Delta H_d Delta^T, Delta = E G, blocked = unblocked, invariance to X
+scaling, GPTQ <= RTN, grid membership, exact ties, pack/unpack and known words.
+No function here is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+from typing import Callable, Dict, Optional
+
+import numpy as np
+
+__all__ = [
+    "hessian", "damp", "inv_chol_upper", "inv_chol_upper_reversed", "prepare_g",
+    "group_params", "quantize_values", "gptq_quantize", "gptq_quantize_obs_literal",
+    "rtn_quantize", "dequantize", "layer_loss", "direct_loss", "pack_codes", "unpack_codes",
+    "quant_range", "TIE_TOL",
+]
+
+TIE_TOL = 1e-3   # a v within this many steps of k + 1/2 is a near-tie (either code accepted)
+
+
+# --------------------------------------------------------------------------- a1, a2, a3
+
+def hessian(X, chunk: int = 4096) -> np.ndarray:
+    """H = 2 * sum_t x_t x_t^T over the calibration tokens ([Q] GPTQ, Hessian; R6).
+
+    X is token-major [n_tok, d] (row t is the layer input x_t); the sum runs in
+    float64 over chunks of tokens.
+    """
+    X = np.asarray(X)
+    n, d = X.shape
+    acc = np.zeros((d, d))
+    for t0 in range(0, n, chunk):
+        xc = X[t0:t0 + chunk].astype(np.float64)
+        acc += xc.T @ xc
+    return 2.0 * acc
+
+
+def damp(H: np.ndarray, frac: float):
+    """H_d = H + lambda*I with lambda = frac * mean(diag H) (R5).  Returns (H_d, lambda)."""
+    H = np.asarray(H, dtype=np.float64)
+    lam = float(frac) * float(np.mean(np.diag(H)))
+    return H + lam * np.eye(H.shape[0]), lam
+
+
+def inv_chol_upper(Hd: np.ndarray) -> np.ndarray:
+    """G = Cholesky(H_d^-1)^T, upper triangular with G^T G = H_d^-1 ([Q] GPTQ, second
+    improvement; R3).  Literal route: explicit inverse, then lower Cholesky, then transpose.
+    Raises numpy.linalg.LinAlgError when H_d is not positive definite."""
+    Hinv = np.linalg.inv(Hd)
+    Hinv = 0.5 * (Hinv + Hinv.T)
+    return np.linalg.cholesky(Hinv).T.copy()
+
+
+def inv_chol_upper_reversed(Hd: np.ndarray) -> np.ndarray:
+    """The same G without forming H_d^-1: factor H_d = U U^T with U upper (a Cholesky of
+    the index-reversed matrix, reversed back), then G = U^-1.  Since H_d^-1 = U^-T U^-1,
+    G = U^-1 is upper with G^T G = H_d^-1, and the factor with positive diagonal is
+    unique, so both routes give the same G."""
+    d = Hd.shape[0]
+    L = np.linalg.cholesky(Hd[::-1, ::-1])
+    U = L[::-1, ::-1]
+    import scipy.linalg
+    return scipy.linalg.solve_triangular(U, np.eye(d), lower=False)
+
+
+def prepare_g(H: np.ndarray, damp_frac: float) -> np.ndarray:
+    """Damping (R5) followed by G = Cholesky(H_d^-1)^T."""
+    Hd, _ = damp(H, damp_frac)
+    return inv_chol_upper(Hd)
+
+
+# --------------------------------------------------------------------------- quantizer
+
+def quant_range(bits: int):
+    """Stored code range [0, 2^b - 1] ([L] 四、量化形式: clip to [qmin, qmax])."""
+    return 0, (1 << bits) - 1
+
+
+def group_params(x: np.ndarray, bits: int, sym: bool):
+    """Scale and zero point of each row of a group (R7, R8, P1).
+
+    x: current values [rows, g] (float64 state).  Returns (s float32 [rows],
+    z int64 [rows], zf float32 [rows]) where zf is the pre-rounding zero point
+    (equal to z for the symmetric form).
+    """
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    maxq = (1 << bits) - 1
+    one = np.float32(1.0)
+    if sym:
+        # [L] 二: [-T, T] maps onto the symmetric integer range; [Q] 量化基础: x_q = round(x/s).
+        amax = np.max(np.abs(x32), axis=1)
+        amax = np.where(amax == 0, one, amax).astype(np.float32)
+        s = (amax / np.float32((1 << (bits - 1)) - 1)).astype(np.float32)
+        z = np.full(x32.shape[0], 1 << (bits - 1), dtype=np.int64)
+        return s, z, z.astype(np.float32)
+    # [Q] 量化基础: asymmetric x_q = round(x/s + z) with zero point z.
+    xmin = np.minimum(np.min(x32, axis=1), np.float32(0))
+    xmax = np.maximum(np.max(x32, axis=1), np.float32(0))
+    deg = xmax == xmin
+    xmin = np.where(deg, np.float32(-1), xmin).astype(np.float32)
+    xmax = np.where(deg, one, xmax).astype(np.float32)
+    s = ((xmax - xmin) / np.float32(maxq)).astype(np.float32)
+    zf = ((-xmin) / s).astype(np.float32)
+    z = np.clip(np.rint(zf), 0, maxq).astype(np.int64)
+    return s, z, zf
+
+
+def quantize_values(w: np.ndarray, s: np.ndarray, z: np.ndarray, bits: int):
+    """code = clip(rne(w/s + z), 0, 2^b - 1) decided in float32 (R9, P1).
+
+    Returns (code int64, v float32 pre-rounding value).
+    """
+    maxq = (1 << bits) - 1
+    w32 = np.asarray(w, dtype=np.float64).astype(np.float32)
+    v = (w32 / s + z.astype(np.float32)).astype(np.float32)
+    code = np.clip(np.rint(v), 0, maxq).astype(np.int64)
+    return code, v
+
+
+def dequantize(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray, g: int) -> np.ndarray:
+    """W^ = s (code - z) in float64 (exact for float32 s and small integers)."""
+    s = np.repeat(np.asarray(scales, dtype=np.float64), g, axis=1)
+    z = np.repeat(np.asarray(zeros, dtype=np.float64), g, axis=1)
+    return s * (np.asarray(codes, dtype=np.float64) - z)
+
+
+def _near_tie(v: np.ndarray, tol: float) -> np.ndarray:
+    f = v.astype(np.float64) - np.floor(v.astype(np.float64))
+    return np.abs(f - 0.5) < tol
+
+
+# --------------------------------------------------------------------------- a4..a6
+
+TieHook = Callable[[str, int, np.ndarray, np.ndarray, np.ndarray, np.ndarray], np.ndarray]
+
+
+def gptq_quantize(W, G: np.ndarray, bits: int, group: int, sym: bool,
+                  block: Optional[int] = None, tie_hook: Optional[TieHook] = None,
+                  tie_tol: float = TIE_TOL) -> Dict[str, np.ndarray]:
+    """Column-by-column quantization with OBS compensation, read through G.
+
+    [Q] GPTQ: for q = 0, 1, ... in fixed order (R4): quantize w_q, then move every
+    not-yet-quantized weight by delta = -(w_q - quant(w_q)) / [H^-1]_qq * H^-1_{:,q}
+    (the inverse over the remaining set, R2).  With G upper and G^T G = H_d^-1 this is
+        e = (w_q - w^_q) / G_qq,     w_k -= e * G_qk   for k > q.
+    block=None applies every update at once (the definition).  block=B restricts the
+    immediate update to the current block of B columns and applies the rest after the
+    block as one product W[:, end:] -= E[:, blk] @ G[blk, end:] ([Q] GPTQ, third
+    improvement, lazy batch update).
+
+    group: 0 means one group per row (per-output-channel, [Q] GPTQ engineering
+    paragraph); g > 0 means runs of g columns ([G]).  (s, z) are set at each group's
+    first column from the current values (R7).
+
+    tie_hook(kind, q, rows, own, lo, hi) is consulted only where the float32 value
+    that decides an integer lies within tie_tol of k + 1/2 (kind "code" or "zero");
+    it returns the value to keep for those rows and must return lo or hi.  It lets a
+    caller check another implementation's choice at such ambiguous points; the
+    arithmetic here never takes values from it.
+
+    Returns codes [d_row, d_col] (stored, in [0, 2^b-1]), scales float32 and zeros
+    [d_row, d_col/g], w_hat float64, E (the e values) float64, V float32 pre-rounding
+    values, W_cur the current value of each weight when it was quantized, ties (number
+    of positions where the hook changed the choice).
+    """
+    Wc = np.array(W, dtype=np.float64, copy=True)
+    d_row, d_col = Wc.shape
+    G = np.asarray(G, dtype=np.float64)
+    if G.shape != (d_col, d_col):
+        raise ValueError("G must be d_col x d_col")
+    g = d_col if group == 0 else int(group)
+    if d_col % g:
+        raise ValueError("group must divide d_col")
+    if block is not None and not (block % g == 0 or g % block == 0):
+        raise ValueError("block and group must nest")
+    maxq = (1 << bits) - 1
+
+    codes = np.zeros((d_row, d_col), np.int64)
+    w_hat = np.zeros((d_row, d_col))
+    E = np.zeros((d_row, d_col))
+    V = np.zeros((d_row, d_col), np.float32)
+    W_cur = np.zeros((d_row, d_col))
+    scales = np.zeros((d_row, d_col // g), np.float32)
+    zeros = np.zeros((d_row, d_col // g), np.int64)
+    ties = 0
+    s = z = None
+    B = d_col if block is None else int(block)
+
+    for j0 in range(0, d_col, B):
+        j1 = min(j0 + B, d_col)
+        for q in range(j0, j1):
+            if q % g == 0:
+                s, z, zf = group_params(Wc[:, q:q + g], bits, sym)
+                if tie_hook is not None and not sym:
+                    amb = np.nonzero(_near_tie(zf, tie_tol))[0]
+                    if amb.size:
+                        lo = np.clip(np.floor(zf[amb]), 0, maxq).astype(np.int64)
+                        hi = np.clip(lo + 1, 0, maxq)
+                        ch = np.asarray(tie_hook("zero", q, amb, z[amb], lo, hi), np.int64)
+                        ties += int(np.count_nonzero(ch != z[amb]))
+                        z = z.copy()
+                        z[amb] = ch
+                scales[:, q // g] = s
+                zeros[:, q // g] = z
+            W_cur[:, q] = Wc[:, q]
+            code, v = quantize_values(Wc[:, q], s, z, bits)
+            if tie_hook is not None:
+                amb = np.nonzero(_near_tie(v, tie_tol))[0]
+                if amb.size:
+                    lo = np.clip(np.floor(v[amb].astype(np.float64)), 0, maxq).astype(np.int64)
+                    hi = np.clip(lo + 1, 0, maxq)
+                    keep = lo != hi
+                    amb, lo, hi = amb[keep], lo[keep], hi[keep]
+                    if amb.size:
+                        ch = np.asarray(tie_hook("code", q, amb, code[amb], lo, hi), np.int64)
+                        ties += int(np.count_nonzero(ch != code[amb]))
+                        code[amb] = ch
+            wq = s.astype(np.float64) * (code - z).astype(np.float64)
+            e = (Wc[:, q] - wq) / G[q, q]
+            codes[:, q] = code
+            w_hat[:, q] = wq
+            E[:, q] = e
+            V[:, q] = v
+            Wc[:, q] = wq
+            # immediate update of the not-yet-quantized columns inside the block
+            Wc[:, q + 1:j1] -= np.outer(e, G[q, q + 1:j1])
+        if j1 < d_col:
+            # lazy batch update of everything right of the block
+            Wc[:, j1:] -= E[:, j0:j1] @ G[j0:j1, j1:]
+
+    return {"codes": codes, "scales": scales, "zeros": zeros, "w_hat": w_hat, "E": E,
+            "V": V, "W_cur": W_cur, "ties": ties, "group": g}
+
+
+def gptq_quantize_obs_literal(W, Hd: np.ndarray, bits: int, group: int, sym: bool):
+    """The OBS step of [Q] GPTQ taken literally, for tiny layers only.
+
+    At column q the remaining set is F = {q, ..., d_col-1}; its inverse Hessian
+    Hinv_F = inv(H_d[F, F]) is formed explicitly and every remaining weight moves by
+    delta_F = -(w_q - quant(w_q)) / [Hinv_F]_qq * [Hinv_F]_{:, q}.  No Cholesky is
+    used, so agreement with gptq_quantize checks the reading R2/R3.
+    """
+    Wc = np.array(W, dtype=np.float64, copy=True)
+    d_row, d_col = Wc.shape
+    g = d_col if group == 0 else int(group)
+    codes = np.zeros((d_row, d_col), np.int64)
+    w_hat = np.zeros((d_row, d_col))
+    s = z = None
+    for q in range(d_col):
+        if q % g == 0:
+            s, z, _ = group_params(Wc[:, q:q + g], bits, sym)
+        code, _ = quantize_values(Wc[:, q], s, z, bits)
+        wq = s.astype(np.float64) * (code - z)
+        Hinv_F = np.linalg.inv(Hd[q:, q:])
+        delta = -np.outer((Wc[:, q] - wq) / Hinv_F[0, 0], Hinv_F[:, 0])
+        Wc[:, q:] += delta
+        codes[:, q] = code
+        w_hat[:, q] = wq
+    return {"codes": codes, "w_hat": w_hat, "W_final": Wc}
+
+
+def rtn_quantize(W, bits: int, group: int, sym: bool) -> Dict[str, np.ndarray]:
+    """Round-to-nearest: the same quantizer on the original weights, no compensation."""
+    W = np.asarray(W, dtype=np.float64)
+    d_row, d_col = W.shape
+    g = d_col if group == 0 else int(group)
+    codes = np.zeros((d_row, d_col), np.int64)
+    scales = np.zeros((d_row, d_col // g), np.float32)
+    zeros = np.zeros((d_row, d_col // g), np.int64)
+    for k in range(d_col // g):
+        cols = slice(k * g, (k + 1) * g)
+        s, z, _ = group_params(W[:, cols], bits, sym)
+        scales[:, k] = s
+        zeros[:, k] = z
+        for c in range(k * g, (k + 1) * g):
+            codes[:, c], _ = quantize_values(W[:, c], s, z, bits)
+    w_hat = dequantize(codes, scales, zeros, g)
+    return {"codes": codes, "scales": scales, "zeros": zeros, "w_hat": w_hat, "group": g}
+
+
+# --------------------------------------------------------------------------- a8
+
+def layer_loss(W, w_hat, H: np.ndarray) -> float:
+    """||W X - W^ X||_F^2 written through H = 2 X X^T: 1/2 * sum_r D_r H D_r^T (R1)."""
+    D = np.asarray(W, dtype=np.float64) - np.asarray(w_hat, dtype=np.float64)
+    return float(0.5 * np.sum((D @ H) * D))
+
+
+def direct_loss(W, w_hat, X) -> float:
+    """The same objective computed from the activations (X token-major [n_tok, d])."""
+    D = np.asarray(W, dtype=np.float64) - np.asarray(w_hat, dtype=np.float64)
+    Y = np.asarray(X, dtype=np.float64) @ D.T
+    return float(np.sum(Y * Y))
+
+
+# --------------------------------------------------------------------------- a7
+
+def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Code (r, c) occupies bits [c*b, c*b + b) of row r's little-endian bitstream,
+    stored as uint32 words [rows, d_col*b/32].  Bit-by-bit, for clarity."""
+    codes = np.asarray(codes, dtype=np.int64)
+    rows, n = codes.shape
+    if (n * bits) % 32:
+        raise ValueError("d_col * bits must be a multiple of 32")
+    words = np.zeros((rows, n * bits // 32), np.uint64)
+    for c in range(n):
+        for k in range(bits):
+            pos = c * bits + k
+            bit = ((codes[:, c] >> k) & 1).astype(np.uint64)
+            words[:, pos // 32] |= bit << np.uint64(pos % 32)
+    return words.astype(np.uint32)
+
+
+def unpack_codes(words: np.ndarray, bits: int, n: int) -> np.ndarray:
+    words = np.asarray(words, dtype=np.uint64)
+    rows = words.shape[0]
+    codes = np.zeros((rows, n), np.int64)
+    for c in range(n):
+        for k in range(bits):
+            pos = c * bits + k
+            bit = (words[:, pos // 32] >> np.uint64(pos % 32)) & np.uint64(1)
+            codes[:, c] |= bit.astype(np.int64) << k
+    return codes
