@@ -1,0 +1,167 @@
+/*
+ * gptq.h - C ABI of the GPTQ layer-quantization library for AMD Instinct MI355X (gfx950).
+ *
+ * One linear layer W [d_row x d_col] (row = output channel, column = input channel) is
+ * quantized column by column, following the GPTQ section of the page "量化"
+ * (Quantization, dingiv.github.io/ai/compute/kernel/quantization):
+ *   objective      argmin_W^ ||W X - W^ X||^2 over the calibration inputs X,
+ *   Hessian        H = 2 X X^T,
+ *   inverse factor G = Cholesky(H^-1)^T (upper triangular, G^T G = H^-1),
+ *   compensation   after quantizing column q, every not-yet-quantized weight of the row
+ *                  moves by -(w_q - quant(w_q)) / [H^-1]_qq * H^-1_{:,q}, read through G,
+ *   order          fixed, left to right,
+ *   blocks         B columns at a time; columns right of the block get one lazy batch
+ *                  update (a matrix product) after the block.
+ * The quantizer is the linear one of section "量化基础" on the same page
+ * (x_q = round(x/s) symmetric, round(x/s + z) asymmetric) with the round-and-clip of
+ * section "四、量化形式" of the LLM-quantization introduction on m.youleyou.com, at one
+ * scale/zero pair per output row or per run of g input columns (granularity table of
+ * the page "大模型常见的量化方式", psvmc.cn).
+ *
+ * Conventions for every call:
+ *   - Matrices are row-major.  Tensor arguments are DEVICE pointers owned by the caller;
+ *     the library keeps no pointer after a call returns and allocates no device memory.
+ *     Scratch memory is the caller's workspace `ws` of at least the size returned by the
+ *     matching *_workspace_size function (16-byte aligned).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All work is
+ *     enqueued on it and the call returns without waiting, except gptq_prepare_hinv with
+ *     a non-NULL `info`, which waits for the stream once to read the pivot flag.
+ *   - Arguments are validated before any HIP call.  Errors are returned as negative codes;
+ *     gptq_last_error() gives a message for the calling thread.  Nothing is written on a
+ *     validation error.  No C++ exception crosses this interface.
+ *   - Results are deterministic: repeated calls on the same inputs give identical bytes.
+ */
+#ifndef GPTQ_H
+#define GPTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define GPTQ_OK 0
+#define GPTQ_EINVAL (-1)  /* bad argument (null pointer, shape, alignment, spec)          */
+#define GPTQ_ENOTSPD (-2) /* damped Hessian not positive definite (a pivot <= 0 or NaN)  */
+#define GPTQ_EHIP (-3)    /* a HIP runtime call failed                                    */
+#define GPTQ_ENOWS (-4)   /* workspace smaller than the size query returned               */
+
+/* element types of W and X */
+#define GPTQ_F16 0
+#define GPTQ_F32 1
+
+/* What to quantize to.
+ *   bits       2, 3, 4 or 8: codes are stored in [0, 2^bits - 1].
+ *   group      0: one (scale, zero) per output row ("per-channel");
+ *              g > 0: one pair per run of g consecutive input columns of a row.
+ *              g must divide d_col, and block % g == 0 or g % block == 0.
+ *   sym        0: asymmetric, range [min(0, min x), max(0, max x)] of the group,
+ *                 s = range / (2^bits - 1), z = round(-min / s);
+ *              1: symmetric, s = max|x| / (2^(bits-1) - 1), z = 2^(bits-1)
+ *                 (signed codes clipped to [-2^(bits-1), 2^(bits-1) - 1], stored + z).
+ *              A group whose range is empty uses the range [-1, 1].
+ *   block      B in {32, 64, 128, 256}: columns quantized with immediate updates
+ *              before the lazy batch update of the columns to their right.
+ *   damp_frac  lambda = damp_frac * mean(diag H) is added to diag H before inversion
+ *              (the pages do not fix a damping; 0.01 is customary).
+ * (s, z) are computed at the first column of each group from the weights as they are
+ * at that moment (after the compensation from all earlier columns).  Codes are
+ * clip(round_half_even(w / s + z), 0, 2^bits - 1), decided in float32 with IEEE
+ * division; the dequantized weight is s * (code - z). */
+typedef struct gptq_spec {
+  int bits;
+  int group;
+  int sym;
+  int block;
+  float damp_frac;
+} gptq_spec;
+
+const char* gptq_version(void);
+const char* gptq_strerror(int code);
+/* Message of the last failed call on this thread ("" if none). */
+const char* gptq_last_error(void);
+
+/* ---------------------------------------------------------------- Hessian (a1)
+ * H += 2 * X^T X, i.e. H[i][j] += 2 * sum_t X[t][i] * X[t][j]  (page "量化", GPTQ:
+ * H = 2 X X^T with X as d x n_tok; here X is stored token-major).
+ *   H      d x d float32, row-major, read and written in full (both triangles receive
+ *          the same value, so a symmetric H stays exactly symmetric).  The caller
+ *          zeroes H before the first chunk; calls on successive token chunks sum up.
+ *   X      n_tok x d, row t = the layer input of token t, leading dimension ldx
+ *          (elements) >= d.  x_dtype GPTQ_F16 (products exact, float32 accumulation)
+ *          or GPTQ_F32.  X and ldx * element size must be 16-byte aligned.
+ *   n_tok  >= 0; 0 is a no-op.
+ * Errors: GPTQ_EINVAL, GPTQ_ENOWS, GPTQ_EHIP. */
+size_t gptq_hessian_workspace_size(int64_t d, int64_t n_tok, int x_dtype);
+int gptq_hessian_accumulate(float* H, int64_t d, const void* X, int x_dtype, int64_t n_tok,
+                            int64_t ldx, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- inverse factor (a2, a3)
+ * G = Cholesky((H + lambda I)^-1)^T with lambda = damp_frac * mean(diag H): G is upper
+ * triangular with positive diagonal and G^T G = (H + lambda I)^-1 (page "量化", GPTQ,
+ * Cholesky reformulation).  Computed without forming the inverse: H + lambda I = U U^T
+ * with U upper, then G = U^-1 (the same unique factor).
+ *   H      d x d float32 symmetric; only its upper triangle is read.
+ *   G      d x d float32 output; the strictly lower triangle is set to 0.  G == H
+ *          (in place) is allowed.
+ *   info   host pointer or NULL.  Non-NULL: the call waits for the stream, sets *info
+ *          to 0 on success or to a positive value when a pivot was <= 0 or not finite,
+ *          and then returns GPTQ_ENOTSPD (G is then undefined).  NULL: no wait and
+ *          no check.
+ * Errors: GPTQ_EINVAL (d < 1, damp_frac < 0 or not finite), GPTQ_ENOWS, GPTQ_ENOTSPD,
+ * GPTQ_EHIP. */
+size_t gptq_prepare_workspace_size(int64_t d);
+int gptq_prepare_hinv(const float* H, float* G, int64_t d, float damp_frac, void* ws,
+                      size_t ws_bytes, int64_t* info, void* stream);
+
+/* ---------------------------------------------------------------- column solve (a4-a7)
+ * Quantizes W with GPTQ given G from gptq_prepare_hinv (page "量化", GPTQ: fixed order,
+ * OBS compensation through G, blocks of spec->block columns with a lazy batch update).
+ *   W         d_row x d_col, w_dtype GPTQ_F16 or GPTQ_F32, not modified (the working
+ *             copy lives in the workspace).  d_col must be a multiple of 32.
+ *   G         d_col x d_col float32 upper triangular (entries below the diagonal unused).
+ *   qweight   d_row x (d_col * bits / 32) uint32 words: code (r, c) occupies bits
+ *             [c*bits, c*bits + bits) of row r's little-endian bit stream.
+ *   scales    d_row x n_groups float32, zeros d_row x n_groups uint8, with
+ *             n_groups = 1 (group 0) or d_col / group.
+ *   err_sq_rows  NULL or d_row doubles: receives sum_q e_q^2 per row, where
+ *             e_q = (w_q - w^_q) / G_qq; equals Delta H_d Delta^T for Delta = W - W^.
+ * Errors: GPTQ_EINVAL, GPTQ_ENOWS, GPTQ_EHIP. */
+size_t gptq_quantize_workspace_size(int64_t d_row, int64_t d_col, const gptq_spec* spec);
+int gptq_quantize_layer(const void* W, int w_dtype, int64_t d_row, int64_t d_col, const float* G,
+                        const gptq_spec* spec, uint32_t* qweight, float* scales, uint8_t* zeros,
+                        double* err_sq_rows, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- check (a8)
+ * Dequantizes W^ = s * (code - z) and measures the layer objective of page "量化", GPTQ,
+ * ||W X - W^ X||_F^2 = 1/2 * sum_r (W - W^)_r H (W - W^)_r^T with the undamped H.
+ *   qweight/scales/zeros  as written by gptq_quantize_layer for the same spec and shape.
+ *   W        the original weights; H the undamped d_col x d_col Hessian.
+ *   loss     device pointer to 1 double (the objective above).
+ *   row_loss NULL or device pointer to d_row doubles (each row's share).
+ *   W_hat    NULL or device d_row x d_col float32 receiving the dequantized weights.
+ *   off_grid device pointer to 1 int64: number of groups whose zero point lies outside
+ *            [0, 2^bits - 1] or whose scale is not finite and positive.
+ * Errors: GPTQ_EINVAL, GPTQ_ENOWS, GPTQ_EHIP. */
+size_t gptq_check_workspace_size(int64_t d_row, int64_t d_col);
+int gptq_dequant_check(const uint32_t* qweight, const float* scales, const uint8_t* zeros,
+                       const void* W, int w_dtype, const float* H, int64_t d_row, int64_t d_col,
+                       const gptq_spec* spec, double* loss, double* row_loss, float* W_hat,
+                       int64_t* off_grid, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- instrumentation
+ * Optional per-kernel timing with HIP events recorded on the caller's stream around
+ * every launch of the named kernel family ("hessian_mfma", "hessian_reduce", "prep",
+ * "quant_block", "lazy_gemm", ...).  Enabling costs two event records per launch.
+ * gptq_profile_read returns the number of timed launches and their summed duration in
+ * milliseconds (waits for the recorded events).  Not thread-safe; for measurement. */
+int gptq_profile_enable(int on);
+int gptq_profile_reset(void);
+int gptq_profile_read(const char* kernel, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPTQ_H */

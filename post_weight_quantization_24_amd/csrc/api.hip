@@ -1,0 +1,282 @@
+// C ABI of libgptq: argument validation (before any HIP call), workspace checks, launch
+// orchestration on the caller's stream, error codes and messages, and the optional
+// per-kernel event timing.  The numerical work lives in hessian.hip, prep.hip,
+// quant.hip, gemm.hip and check.hip.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+#include <climits>
+
+#include "gptq.h"
+#include "gptq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(GPTQ_EHIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---------------------------------------------------------------- instrumentation
+struct PendingEvent {
+  std::string name;
+  hipEvent_t e0, e1;
+};
+struct ProfTotal {
+  int64_t launches = 0;
+  double ms = 0.0;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<PendingEvent> g_pending;
+std::map<std::string, ProfTotal> g_totals;
+
+void drain_pending() {
+  for (auto& p : g_pending) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(p.e1) == hipSuccess && hipEventElapsedTime(&ms, p.e0, p.e1) == hipSuccess) {
+      auto& t = g_totals[p.name];
+      t.launches += 1;
+      t.ms += ms;
+    }
+    (void)hipEventDestroy(p.e0);
+    (void)hipEventDestroy(p.e1);
+  }
+  g_pending.clear();
+}
+
+int check_spec(const gptq_spec* spec, int64_t d_col) {
+  if (!spec) return fail(GPTQ_EINVAL, "spec is NULL");
+  if (spec->bits != 2 && spec->bits != 3 && spec->bits != 4 && spec->bits != 8)
+    return fail(GPTQ_EINVAL, "bits must be 2, 3, 4 or 8 (got %d)", spec->bits);
+  if (spec->block != 32 && spec->block != 64 && spec->block != 128 && spec->block != 256)
+    return fail(GPTQ_EINVAL, "block must be 32, 64, 128 or 256 (got %d)", spec->block);
+  if (spec->sym != 0 && spec->sym != 1) return fail(GPTQ_EINVAL, "sym must be 0 or 1");
+  if (spec->group < 0) return fail(GPTQ_EINVAL, "group must be >= 0");
+  if (spec->group > 0) {
+    if (spec->group % 16 != 0)
+      return fail(GPTQ_EINVAL, "group must be a multiple of 16 (got %d)", spec->group);
+    if (d_col % spec->group != 0)
+      return fail(GPTQ_EINVAL, "group %d does not divide d_col %lld", spec->group, (long long)d_col);
+    if (spec->block % spec->group != 0 && spec->group % spec->block != 0)
+      return fail(GPTQ_EINVAL, "block %d and group %d must nest", spec->block, spec->group);
+  }
+  return GPTQ_OK;
+}
+
+int check_layer(int w_dtype, int64_t d_row, int64_t d_col) {
+  if (w_dtype != GPTQ_F16 && w_dtype != GPTQ_F32) return fail(GPTQ_EINVAL, "w_dtype must be F16 or F32");
+  if (d_row < 1 || d_row > (int64_t)1 << 30) return fail(GPTQ_EINVAL, "d_row out of range");
+  if (d_col < 32 || d_col % 32 != 0 || d_col > (int64_t)1 << 20)
+    return fail(GPTQ_EINVAL, "d_col must be a positive multiple of 32 (got %lld)", (long long)d_col);
+  return GPTQ_OK;
+}
+
+}  // namespace
+
+namespace gptq {
+
+ProfScope::ProfScope(const char* n, hipStream_t s) : name(n), stream(s), ev0(nullptr) {
+  if (!g_prof_on) return;
+  hipEvent_t e;
+  if (hipEventCreate(&e) != hipSuccess) return;
+  if (hipEventRecord(e, s) != hipSuccess) {
+    (void)hipEventDestroy(e);
+    return;
+  }
+  ev0 = e;
+}
+
+ProfScope::~ProfScope() {
+  if (!ev0) return;
+  hipEvent_t e1;
+  if (hipEventCreate(&e1) != hipSuccess || hipEventRecord(e1, stream) != hipSuccess) {
+    (void)hipEventDestroy(static_cast<hipEvent_t>(ev0));
+    return;
+  }
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_pending.push_back({name, static_cast<hipEvent_t>(ev0), e1});
+}
+
+}  // namespace gptq
+
+extern "C" {
+
+const char* gptq_version(void) { return "gptq-mi355x 0.1.0 (gfx950)"; }
+
+const char* gptq_strerror(int code) {
+  switch (code) {
+    case GPTQ_OK: return "ok";
+    case GPTQ_EINVAL: return "invalid argument";
+    case GPTQ_ENOTSPD: return "damped Hessian is not positive definite";
+    case GPTQ_EHIP: return "HIP runtime error";
+    case GPTQ_ENOWS: return "workspace too small";
+    default: return "unknown error";
+  }
+}
+
+const char* gptq_last_error(void) { return g_last_error.c_str(); }
+
+// ---------------------------------------------------------------- Hessian
+size_t gptq_hessian_workspace_size(int64_t d, int64_t n_tok, int x_dtype) {
+  if (d < 1 || n_tok < 1 || (x_dtype != GPTQ_F16 && x_dtype != GPTQ_F32)) return 0;
+  return gptq::hessian_plan(d, n_tok, x_dtype).ws_bytes;
+}
+
+int gptq_hessian_accumulate(float* H, int64_t d, const void* X, int x_dtype, int64_t n_tok,
+                            int64_t ldx, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (d < 1 || d > (int64_t)1 << 20) return fail(GPTQ_EINVAL, "d out of range (%lld)", (long long)d);
+  if (n_tok < 0) return fail(GPTQ_EINVAL, "n_tok < 0");
+  if (x_dtype != GPTQ_F16 && x_dtype != GPTQ_F32) return fail(GPTQ_EINVAL, "x_dtype must be F16 or F32");
+  if (!H) return fail(GPTQ_EINVAL, "H is NULL");
+  if (n_tok == 0) return GPTQ_OK;
+  if (!X) return fail(GPTQ_EINVAL, "X is NULL");
+  if (ldx < d) return fail(GPTQ_EINVAL, "ldx (%lld) < d (%lld)", (long long)ldx, (long long)d);
+  const size_t elt = x_dtype == GPTQ_F16 ? 2 : 4;
+  if (!aligned(X, 16) || (ldx * (int64_t)elt) % 16 != 0)
+    return fail(GPTQ_EINVAL, "X and its rows must be 16-byte aligned");
+  const gptq::HessPlan p = gptq::hessian_plan(d, n_tok, x_dtype);
+  if (!ws || ws_bytes < p.ws_bytes)
+    return fail(GPTQ_ENOWS, "workspace of %zu bytes needed", p.ws_bytes);
+  if (!aligned(ws, 16)) return fail(GPTQ_EINVAL, "workspace must be 16-byte aligned");
+  hipError_t e = gptq::hessian_launch(p, H, X, x_dtype, ldx, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gptq_hessian_accumulate");
+  return GPTQ_OK;
+}
+
+// ---------------------------------------------------------------- inverse factor
+size_t gptq_prepare_workspace_size(int64_t d) {
+  if (d < 1) return 0;
+  return gptq::prepare_ws_bytes(d);
+}
+
+int gptq_prepare_hinv(const float* H, float* G, int64_t d, float damp_frac, void* ws,
+                      size_t ws_bytes, int64_t* info, void* stream) {
+  g_last_error.clear();
+  if (d < 1 || d > (int64_t)1 << 20) return fail(GPTQ_EINVAL, "d out of range (%lld)", (long long)d);
+  if (!H || !G) return fail(GPTQ_EINVAL, "H or G is NULL");
+  if (!(damp_frac >= 0.0f) || !std::isfinite(damp_frac))
+    return fail(GPTQ_EINVAL, "damp_frac must be finite and >= 0");
+  const size_t need = gptq::prepare_ws_bytes(d);
+  if (!ws || ws_bytes < need) return fail(GPTQ_ENOWS, "workspace of %zu bytes needed", need);
+  if (!aligned(ws, 256)) return fail(GPTQ_EINVAL, "workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = gptq::prepare_launch(H, G, d, damp_frac, ws, s);
+  if (e != hipSuccess) return hip_fail(e, "gptq_prepare_hinv");
+  if (info) {
+    *info = 0;
+    int flag = INT_MAX;
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "gptq_prepare_hinv sync");
+    if ((e = hipMemcpy(&flag, gptq::prepare_flag_ptr(ws, d), sizeof(int), hipMemcpyDeviceToHost)) !=
+        hipSuccess)
+      return hip_fail(e, "gptq_prepare_hinv flag");
+    if (flag != INT_MAX) {
+      *info = flag;
+      return fail(GPTQ_ENOTSPD, "damped Hessian not positive definite (pivot %d)", flag);
+    }
+  }
+  return GPTQ_OK;
+}
+
+// ---------------------------------------------------------------- column solve
+size_t gptq_quantize_workspace_size(int64_t d_row, int64_t d_col, const gptq_spec* spec) {
+  if (check_layer(GPTQ_F32, d_row, d_col) != GPTQ_OK || check_spec(spec, d_col) != GPTQ_OK) {
+    g_last_error.clear();
+    return 0;
+  }
+  return gptq::quant_ws_bytes(d_row, d_col, spec->block);
+}
+
+int gptq_quantize_layer(const void* W, int w_dtype, int64_t d_row, int64_t d_col, const float* G,
+                        const gptq_spec* spec, uint32_t* qweight, float* scales, uint8_t* zeros,
+                        double* err_sq_rows, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  int rc;
+  if ((rc = check_layer(w_dtype, d_row, d_col)) != GPTQ_OK) return rc;
+  if ((rc = check_spec(spec, d_col)) != GPTQ_OK) return rc;
+  if (!W || !G || !qweight || !scales || !zeros)
+    return fail(GPTQ_EINVAL, "W, G, qweight, scales and zeros must not be NULL");
+  const size_t need = gptq::quant_ws_bytes(d_row, d_col, spec->block);
+  if (!ws || ws_bytes < need) return fail(GPTQ_ENOWS, "workspace of %zu bytes needed", need);
+  if (!aligned(ws, 256)) return fail(GPTQ_EINVAL, "workspace must be 256-byte aligned");
+  gptq::QuantArgs a{W, w_dtype, d_row, d_col, G, spec->bits, spec->group, spec->sym, spec->block,
+                    qweight, scales, zeros, err_sq_rows};
+  hipError_t e = gptq::quant_launch(a, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gptq_quantize_layer");
+  return GPTQ_OK;
+}
+
+// ---------------------------------------------------------------- check
+size_t gptq_check_workspace_size(int64_t d_row, int64_t d_col) {
+  if (check_layer(GPTQ_F32, d_row, d_col) != GPTQ_OK) {
+    g_last_error.clear();
+    return 0;
+  }
+  return gptq::check_ws_bytes(d_row, d_col);
+}
+
+int gptq_dequant_check(const uint32_t* qweight, const float* scales, const uint8_t* zeros,
+                       const void* W, int w_dtype, const float* H, int64_t d_row, int64_t d_col,
+                       const gptq_spec* spec, double* loss, double* row_loss, float* W_hat,
+                       int64_t* off_grid, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  int rc;
+  if ((rc = check_layer(w_dtype, d_row, d_col)) != GPTQ_OK) return rc;
+  if ((rc = check_spec(spec, d_col)) != GPTQ_OK) return rc;
+  if (!qweight || !scales || !zeros || !W || !H || !loss || !off_grid)
+    return fail(GPTQ_EINVAL, "qweight, scales, zeros, W, H, loss and off_grid must not be NULL");
+  const size_t need = gptq::check_ws_bytes(d_row, d_col);
+  if (!ws || ws_bytes < need) return fail(GPTQ_ENOWS, "workspace of %zu bytes needed", need);
+  if (!aligned(ws, 256)) return fail(GPTQ_EINVAL, "workspace must be 256-byte aligned");
+  hipError_t e = gptq::check_launch(qweight, scales, zeros, W, w_dtype, H, d_row, d_col, spec->bits,
+                                    spec->group, loss, row_loss, W_hat, off_grid, ws,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gptq_dequant_check");
+  return GPTQ_OK;
+}
+
+// ---------------------------------------------------------------- instrumentation
+int gptq_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return GPTQ_OK;
+}
+
+int gptq_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  drain_pending();
+  g_totals.clear();
+  return GPTQ_OK;
+}
+
+int gptq_profile_read(const char* kernel, int64_t* launches, double* total_ms) {
+  if (!kernel || !launches || !total_ms) return fail(GPTQ_EINVAL, "NULL argument");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  drain_pending();
+  auto it = g_totals.find(kernel);
+  *launches = it == g_totals.end() ? 0 : it->second.launches;
+  *total_ms = it == g_totals.end() ? 0.0 : it->second.ms;
+  return GPTQ_OK;
+}
+
+}  // extern "C"

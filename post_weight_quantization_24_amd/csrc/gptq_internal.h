@@ -1,0 +1,80 @@
+// Internal declarations shared by the HIP sources of libgptq (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gptq {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- instrumentation
+// Records HIP events around a launch when profiling is on (see gptq_profile_enable).
+struct ProfScope {
+  const char* name;
+  hipStream_t stream;
+  void* ev0;
+  ProfScope(const char* n, hipStream_t s);
+  ~ProfScope();
+};
+
+// ---------------------------------------------------------------- Hessian (hessian.hip)
+// Lower-triangle tiles of 256x256, split over token ranges into partial tiles.
+struct HessPlan {
+  int64_t d, n_tok;
+  int tiles;        // number of lower-triangle 256x256 tiles
+  int splits;       // token ranges
+  int64_t tok_per_split;
+  size_t ws_bytes;
+};
+HessPlan hessian_plan(int64_t d, int64_t n_tok, int x_dtype);
+hipError_t hessian_launch(const HessPlan& p, float* H, const void* X, int x_dtype, int64_t ldx,
+                          void* ws, hipStream_t stream);
+
+// ---------------------------------------------------------------- fp32 MFMA GEMM (gemm.hip)
+// C[MxN] = alpha * op(A) op(B) + beta * C.
+//   op(A)[m][k] = transA ? A[k*lda + m] : A[m*lda + k]
+//   op(B)[k][n] = transB ? B[n*ldb + k] : B[k*ldb + n]
+//   triA: 0 none, 1 op(A) upper (entries with k < m are zero), 2 lower (k > m zero)
+//   triB: 0 none, 1 op(B) upper (k > n zero), 2 lower (k < n zero)
+//   triC: 0 all of C, 1 only entries with m <= n are computed and written.
+// Entries an operand mask declares zero are never read.  beta is 0 or 1.
+struct GemmArgs {
+  int64_t M, N, K;
+  const float* A; int64_t lda; int transA; int triA;
+  const float* B; int64_t ldb; int transB; int triB;
+  float* C; int64_t ldc; int triC;
+  float alpha, beta;
+};
+hipError_t gemm_f32(const GemmArgs& g, hipStream_t stream, const char* prof_name);
+
+// ---------------------------------------------------------------- prepare (prep.hip)
+size_t prepare_ws_bytes(int64_t d);
+hipError_t prepare_launch(const float* H, float* G, int64_t d, float damp_frac, void* ws,
+                          hipStream_t stream);
+// Device flag written by the prepare kernels: 0 ok, else 1 + first failing block row.
+int* prepare_flag_ptr(void* ws, int64_t d);
+
+// ---------------------------------------------------------------- column solve (quant.hip)
+struct QuantArgs {
+  const void* W; int w_dtype; int64_t d_row, d_col;
+  const float* G;
+  int bits, group, sym, block;
+  uint32_t* qweight; float* scales; uint8_t* zeros; double* err_sq_rows;
+};
+size_t quant_ws_bytes(int64_t d_row, int64_t d_col, int block);
+hipError_t quant_launch(const QuantArgs& a, void* ws, hipStream_t stream);
+
+// ---------------------------------------------------------------- check (check.hip)
+size_t check_ws_bytes(int64_t d_row, int64_t d_col);
+hipError_t check_launch(const uint32_t* qweight, const float* scales, const uint8_t* zeros,
+                        const void* W, int w_dtype, const float* H, int64_t d_row, int64_t d_col,
+                        int bits, int group, double* loss, double* row_loss, float* W_hat,
+                        int64_t* off_grid, void* ws, hipStream_t stream);
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
+
+}  // namespace gptq

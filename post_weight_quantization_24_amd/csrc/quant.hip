@@ -1,0 +1,349 @@
+// GPTQ column solve (page "量化", section GPTQ): columns in fixed left-to-right order;
+// after quantizing column q every not-yet-quantized weight of the row moves by
+// -(w_q - quant(w_q)) / [H^-1]_qq * H^-1_{:,q}, which through G = Cholesky(H^-1)^T is
+//     e = (w_q - w^_q) / G_qq,   w_k -= e * G_qk  (k > q).
+// Blocks of B columns: updates inside the block are immediate (quant_block), the columns
+// right of the block get one batch update W[:, end:] -= E G[blk, end:] (fp32 MFMA GEMM).
+//
+// Quantizer (section 量化基础 of the same page; round and clip of the linear form on
+// the m.youleyou.com introduction, section 四): code = clip(rne(w/s + z), 0, 2^b - 1),
+// with (s, z) per row and group of g columns (granularity table on psvmc.cn), computed
+// at the group's first column from the current weights.  Every decision that yields an
+// integer is taken in float32 with IEEE division.
+//
+// quant_block layout: a wave holds 4 rows; each row is spread over a DPP row of 16
+// lanes, lane c owning block columns c, c+16, c+32, ... in registers.  The B x B block
+// of G sits in LDS, stored [q][slot][lane] and only for slots that can still change, so
+// each lane reads its update coefficients conflict-free (the four rows of a wave read
+// the same addresses).  Column q is quantized by its owner lane; its e reaches the
+// other 15 lanes with one DPP row broadcast.
+
+#include <utility>
+
+#include "gptq_internal.h"
+
+namespace gptq {
+
+namespace {
+
+constexpr int LPR = 16;            // lanes per row
+constexpr int ROWS_PER_WG = 16;    // 4 waves x 4 rows
+
+__global__ void __launch_bounds__(256)
+convert_w(const void* __restrict__ W, int w_dtype, int64_t n, float* __restrict__ Wc) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    Wc[i] = w_dtype == 0 ? (float)static_cast<const _Float16*>(W)[i]
+                         : static_cast<const float*>(W)[i];
+}
+
+__global__ void __launch_bounds__(256) zero_f64(double* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0.0;
+}
+
+struct Params {
+  float s;
+  float z;
+};
+
+// (s, z) from the group's min and max (already including 0 for the asymmetric form).
+__device__ __forceinline__ Params make_params(float mn, float mx, int bits, int sym) {
+  const int maxq = (1 << bits) - 1;
+  Params p;
+  if (sym) {
+    float amax = fmaxf(mx, -mn);
+    if (amax == 0.0f) amax = 1.0f;
+    p.s = __fdiv_rn(amax, (float)((1 << (bits - 1)) - 1));
+    p.z = (float)(1 << (bits - 1));
+  } else {
+    float lo = fminf(mn, 0.0f), hi = fmaxf(mx, 0.0f);
+    if (lo == hi) {
+      lo = -1.0f;
+      hi = 1.0f;
+    }
+    p.s = __fdiv_rn(hi - lo, (float)maxq);
+    const float zf = __fdiv_rn(-lo, p.s);
+    p.z = fminf(fmaxf(__builtin_rintf(zf), 0.0f), (float)maxq);
+  }
+  return p;
+}
+
+// One wave per row: parameters of the group [c0, c0 + g) from the current weights.
+__global__ void __launch_bounds__(256)
+group_params(const float* __restrict__ Wc, int64_t d_row, int64_t d_col, int64_t c0, int64_t g,
+             int bits, int sym, float* __restrict__ scales, uint8_t* __restrict__ zeros,
+             int64_t n_groups) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= d_row) return;
+  const float* w = Wc + row * d_col + c0;
+  float mn = 3.0e38f, mx = -3.0e38f;
+  for (int64_t c = lane; c < g; c += 64) {
+    const float x = w[c];
+    mn = fminf(mn, x);
+    mx = fmaxf(mx, x);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, off));
+    mx = fmaxf(mx, __shfl_xor(mx, off));
+  }
+  if (lane == 0) {
+    const Params p = make_params(mn, mx, bits, sym);
+    scales[row * n_groups + c0 / g] = p.s;
+    zeros[row * n_groups + c0 / g] = (uint8_t)p.z;
+  }
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// min / max over the 16 lanes of a DPP row (row_ror:8, 4, 2, 1)
+__device__ __forceinline__ float row_min(float v) {
+  v = fminf(v, dpp<0x128>(v));
+  v = fminf(v, dpp<0x124>(v));
+  v = fminf(v, dpp<0x122>(v));
+  return fminf(v, dpp<0x121>(v));
+}
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, dpp<0x128>(v));
+  v = fmaxf(v, dpp<0x124>(v));
+  v = fmaxf(v, dpp<0x122>(v));
+  return fmaxf(v, dpp<0x121>(v));
+}
+
+// LDS offset of row q of the compact G block: rows q in [16a, 16a+16) keep slots a..S-1.
+template <int B>
+__host__ __device__ constexpr int grow_off(int q) {
+  constexpr int S = B / LPR;
+  const int a = q / LPR;
+  return LPR * LPR * (a * S - a * (a - 1) / 2) + (q - LPR * a) * LPR * (S - a);
+}
+template <int B>
+constexpr int g_lds_floats() { return grow_off<B>(B); }
+
+template <int B>
+struct Row {
+  static constexpr int S = B / LPR;
+  float w[S];      // current weights of the owned columns
+  Params p;
+  float esq;
+};
+
+template <int B, int Q>
+__device__ __forceinline__ void quant_step(Row<B>& r, const float* __restrict__ gl,
+                                           const float* __restrict__ rinv, int c, int bits,
+                                           int sym, int64_t g, int width, int64_t j0,
+                                           float* __restrict__ scales, uint8_t* __restrict__ zeros,
+                                           int64_t n_groups, int64_t row, bool row_ok,
+                                           uint8_t* __restrict__ crow, float* __restrict__ erow) {
+  constexpr int S = B / LPR;
+  constexpr int A = Q / LPR;   // slot holding column Q
+  constexpr int O = Q % LPR;   // owner lane
+  const int maxq = (1 << bits) - 1;
+  // groups are multiples of 16 columns, so a group can only start at a multiple of 16
+  if (O == 0 && g <= B && (Q % g) == 0 && Q < width) {
+    // group [Q, Q + g) inside the block: min / max of the current values
+    float mn = 3.0e38f, mx = -3.0e38f;
+#pragma unroll
+    for (int s = A; s < S; ++s) {
+      const int col = s * LPR + c;
+      if (col >= Q && col < Q + g) {
+        mn = fminf(mn, r.w[s]);
+        mx = fmaxf(mx, r.w[s]);
+      }
+    }
+    mn = row_min(mn);
+    mx = row_max(mx);
+    r.p = make_params(mn, mx, bits, sym);
+    if (c == 0 && row_ok) {
+      const int64_t gi = (j0 + Q) / g;
+      scales[row * n_groups + gi] = r.p.s;
+      zeros[row * n_groups + gi] = (uint8_t)r.p.z;
+    }
+  }
+  const float x = r.w[A];
+  const float v = __fdiv_rn(x, r.p.s) + r.p.z;
+  const float code = fminf(fmaxf(__builtin_rintf(v), 0.0f), (float)maxq);
+  const float wq = r.p.s * (code - r.p.z);
+  float e = (x - wq) * rinv[Q];
+  e = dpp<0x150 + O>(e);  // row_newbcast: every lane of the row takes the owner's e
+  if (Q >= width) e = 0.0f;
+  if (c == O) {
+    crow[Q] = (uint8_t)code;       // LDS, packed after the block
+    if (row_ok) erow[Q] = e;       // E for the lazy update
+  }
+  r.esq = fmaf(e, e, r.esq);
+  const float* gq = gl + grow_off<B>(Q);
+#pragma unroll
+  for (int s = A; s < S; ++s) r.w[s] = fmaf(-e, gq[(s - A) * LPR + c], r.w[s]);
+  // keep later steps' LDS loads from being hoisted here (they would each hold a register)
+  __asm__ volatile("" ::: "memory");
+}
+
+template <int B, int... Qs>
+__device__ __forceinline__ void quant_steps(Row<B>& r, const float* gl, const float* rinv, int c,
+                                            int bits, int sym, int64_t g, int width, int64_t j0,
+                                            float* scales, uint8_t* zeros, int64_t n_groups,
+                                            int64_t row, bool row_ok, uint8_t* crow, float* erow,
+                                            std::integer_sequence<int, Qs...>) {
+  (quant_step<B, Qs>(r, gl, rinv, c, bits, sym, g, width, j0, scales, zeros, n_groups, row,
+                     row_ok, crow, erow),
+   ...);
+}
+
+template <int B>
+__global__ void __launch_bounds__(256)
+quant_block(const float* __restrict__ Wc, const float* __restrict__ G, int64_t d_row,
+            int64_t d_col, int64_t j0, int width, int bits, int sym, int64_t g,
+            float* __restrict__ scales, uint8_t* __restrict__ zeros, int64_t n_groups,
+            uint32_t* __restrict__ qweight, float* __restrict__ E, double* __restrict__ err_sq) {
+  constexpr int S = B / LPR;
+  extern __shared__ float smem[];
+  float* gl = smem;                          // compact G block
+  float* rinv = smem + g_lds_floats<B>();    // 1 / G_qq
+  uint8_t* cbuf = reinterpret_cast<uint8_t*>(rinv + B);  // codes [ROWS_PER_WG][B]
+
+  // stage G[j0 + q][j0 + s*16 + c] for columns > q (0 elsewhere)
+  for (int q = threadIdx.x / LPR; q < B; q += 256 / LPR) {
+    const int c = threadIdx.x % LPR;
+    const int a = q / LPR;
+    float* dst = gl + grow_off<B>(q);
+    for (int s = a; s < S; ++s) {
+      const int k = s * LPR + c;
+      dst[(s - a) * LPR + c] =
+          (k > q && k < width && q < width) ? G[(j0 + q) * d_col + j0 + k] : 0.0f;
+    }
+  }
+  for (int q = threadIdx.x; q < B; q += 256)
+    rinv[q] = q < width ? 1.0f / G[(j0 + q) * d_col + j0 + q] : 0.0f;
+
+  const int c = threadIdx.x % LPR;
+  const int rl = threadIdx.x / LPR;  // row within the workgroup
+  const int64_t row = (int64_t)blockIdx.x * ROWS_PER_WG + rl;
+  const bool row_ok = row < d_row;
+  Row<B> r;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int k = s * LPR + c;
+    r.w[s] = (row_ok && k < width) ? Wc[row * d_col + j0 + k] : 0.0f;
+  }
+  r.esq = 0.0f;
+  if (g > B) {
+    const int64_t gi = j0 / g;
+    r.p.s = row_ok ? scales[row * n_groups + gi] : 1.0f;
+    r.p.z = row_ok ? (float)zeros[row * n_groups + gi] : 0.0f;
+  } else {
+    r.p.s = 1.0f;
+    r.p.z = 0.0f;
+  }
+  __syncthreads();
+
+  quant_steps<B>(r, gl, rinv, c, bits, sym, g, width, j0, scales, zeros, n_groups, row, row_ok,
+                 cbuf + rl * B, E + (row_ok ? row : 0) * B, std::make_integer_sequence<int, B>{});
+
+  if (row_ok && c == 0 && err_sq) err_sq[row] += (double)r.esq;
+  // pack: each lane assembles whole 32-bit words from the row's code bytes in LDS
+  __syncthreads();
+  if (row_ok) {
+    const int nw = width * bits / 32;
+    const int64_t words_per_row = d_col * bits / 32;
+    uint32_t* out = qweight + row * words_per_row + j0 * bits / 32;
+    for (int wi = c; wi < nw; wi += LPR) {
+      const int b0 = wi * 32;
+      const int col_lo = b0 / bits, col_hi = (b0 + 31) / bits;
+      uint32_t word = 0;
+      for (int col = col_lo; col <= col_hi; ++col) {
+        const uint32_t code = cbuf[rl * B + col];
+        const int sh = col * bits - b0;
+        word |= sh >= 0 ? (code << sh) : (code >> (-sh));
+      }
+      out[wi] = word;
+    }
+  }
+}
+
+template <int B>
+size_t quant_block_lds() {
+  return (size_t)(g_lds_floats<B>() + B) * sizeof(float) + ROWS_PER_WG * B;
+}
+
+template <int B>
+hipError_t launch_block(const QuantArgs& a, const float* Wc, float* E, int64_t j0, int width,
+                        hipStream_t s) {
+  static bool attr = false;
+  const size_t lds = quant_block_lds<B>();
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(quant_block<B>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int64_t g = a.group == 0 ? a.d_col : a.group;
+  const int64_t n_groups = a.d_col / g;
+  const int64_t grid = ceil_div(a.d_row, ROWS_PER_WG);
+  hipLaunchKernelGGL(quant_block<B>, dim3((unsigned)grid), dim3(256), lds, s, Wc, a.G, a.d_row,
+                     a.d_col, j0, width, a.bits, a.sym, g, a.scales, a.zeros, n_groups,
+                     a.qweight, E, a.err_sq_rows);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t quant_ws_bytes(int64_t d_row, int64_t d_col, int block) {
+  return align_up((size_t)d_row * d_col * sizeof(float), 256) +
+         align_up((size_t)d_row * block * sizeof(float), 256);
+}
+
+hipError_t quant_launch(const QuantArgs& a, void* ws, hipStream_t s) {
+  hipError_t e;
+  float* Wc = static_cast<float*>(ws);
+  float* E = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                      align_up((size_t)a.d_row * a.d_col * sizeof(float), 256));
+  const int64_t n = a.d_row * a.d_col;
+  const int64_t g = a.group == 0 ? a.d_col : a.group;
+  const int64_t n_groups = a.d_col / g;
+  {
+    ProfScope ps("quant_convert", s);
+    const int64_t grid = ceil_div(n, 256) < 4096 ? ceil_div(n, 256) : 4096;
+    hipLaunchKernelGGL(convert_w, dim3((unsigned)grid), dim3(256), 0, s, a.W, a.w_dtype, n, Wc);
+    if (a.err_sq_rows) {
+      const int64_t gz = ceil_div(a.d_row, 256) < 1024 ? ceil_div(a.d_row, 256) : 1024;
+      hipLaunchKernelGGL(zero_f64, dim3((unsigned)gz), dim3(256), 0, s, a.err_sq_rows, a.d_row);
+    }
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  for (int64_t j0 = 0; j0 < a.d_col; j0 += a.block) {
+    const int width = (int)(a.d_col - j0 < a.block ? a.d_col - j0 : a.block);
+    if (g > a.block && j0 % g == 0) {
+      ProfScope ps("quant_group_params", s);
+      hipLaunchKernelGGL(group_params, dim3((unsigned)ceil_div(a.d_row, 4)), dim3(256), 0, s, Wc,
+                         a.d_row, a.d_col, j0, g, a.bits, a.sym, a.scales, a.zeros, n_groups);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    {
+      ProfScope ps("quant_block", s);
+      switch (a.block) {
+        case 32: e = launch_block<32>(a, Wc, E, j0, width, s); break;
+        case 64: e = launch_block<64>(a, Wc, E, j0, width, s); break;
+        case 128: e = launch_block<128>(a, Wc, E, j0, width, s); break;
+        case 256: e = launch_block<256>(a, Wc, E, j0, width, s); break;
+        default: e = hipErrorInvalidValue;
+      }
+      if (e != hipSuccess) return e;
+    }
+    const int64_t rest = a.d_col - j0 - width;
+    if (rest > 0) {
+      // W[:, j0+w:] -= E[:, :w] G[j0:j0+w, j0+w:]
+      GemmArgs ga{a.d_row, rest, width, E, a.block, 0, 0,
+                  a.G + j0 * a.d_col + j0 + width, a.d_col, 0, 0,
+                  Wc + j0 + width, a.d_col, 0, -1.0f, 1.0f};
+      if ((e = gemm_f32(ga, s, "lazy_gemm")) != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace gptq

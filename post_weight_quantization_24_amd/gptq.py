@@ -1,0 +1,213 @@
+"""Thin ctypes binding of libgptq (include/gptq.h).  Argument marshalling only: every step
+of the quantization runs in the HIP library; torch supplies device memory and streams.
+
+The binding raises GptqError for a negative return code, with the library's message.
+If libgptq.so is missing the first call raises: there is no other implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgptq.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "gptq.h")
+
+OK, EINVAL, ENOTSPD, EHIP, ENOWS = 0, -1, -2, -3, -4
+F16, F32 = 0, 1
+
+
+class GptqError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("%s (code %d)" % (msg, code))
+        self.code = code
+
+
+class Spec(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int), ("group", ctypes.c_int), ("sym", ctypes.c_int),
+                ("block", ctypes.c_int), ("damp_frac", ctypes.c_float)]
+
+    @classmethod
+    def make(cls, bits=4, group=128, sym=False, block=128, damp_frac=0.01):
+        return cls(int(bits), int(group), int(bool(sym)), int(block), float(damp_frac))
+
+
+_lib = None
+_vp, _i64, _sz, _int, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int, ctypes.c_float
+_SIGS = {
+    "gptq_version": ([], ctypes.c_char_p),
+    "gptq_strerror": ([_int], ctypes.c_char_p),
+    "gptq_last_error": ([], ctypes.c_char_p),
+    "gptq_hessian_workspace_size": ([_i64, _i64, _int], _sz),
+    "gptq_hessian_accumulate": ([_vp, _i64, _vp, _int, _i64, _i64, _vp, _sz, _vp], _int),
+    "gptq_prepare_workspace_size": ([_i64], _sz),
+    "gptq_prepare_hinv": ([_vp, _vp, _i64, _f32, _vp, _sz, ctypes.POINTER(_i64), _vp], _int),
+    "gptq_quantize_workspace_size": ([_i64, _i64, ctypes.POINTER(Spec)], _sz),
+    "gptq_quantize_layer": ([_vp, _int, _i64, _i64, _vp, ctypes.POINTER(Spec), _vp, _vp, _vp, _vp,
+                             _vp, _sz, _vp], _int),
+    "gptq_check_workspace_size": ([_i64, _i64], _sz),
+    "gptq_dequant_check": ([_vp, _vp, _vp, _vp, _int, _vp, _i64, _i64, ctypes.POINTER(Spec), _vp,
+                            _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "gptq_profile_enable": ([_int], _int),
+    "gptq_profile_reset": ([], _int),
+    "gptq_profile_read": ([ctypes.c_char_p, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double)], _int),
+}
+
+
+def lib():
+    """The loaded library; raises if libgptq.so has not been built.
+
+    torch is imported first: its wheel carries its own HIP runtime under the same soname,
+    and loading it first makes libgptq bind to that one instance instead of starting a
+    second HIP runtime in the process (which then sees no device)."""
+    global _lib
+    if _lib is None:
+        import torch  # noqa: F401
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libgptq.so not found at %s: build it with "
+                               "`python -m post_weight_quantization_24_amd.build_lib`" % LIB_PATH)
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(l, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = l
+    return _lib
+
+
+def header_functions():
+    """Names of the functions declared in include/gptq.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(gptq_\w+)\s*\(", text, re.M)))
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise GptqError(rc, lib().gptq_last_error().decode() or lib().gptq_strerror(rc).decode())
+
+
+def version() -> str:
+    return lib().gptq_version().decode()
+
+
+# ------------------------------------------------------------------ torch-facing helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError("expected float16 or float32, got %s" % t.dtype)
+
+
+def _workspace(nbytes: int, device, ws=None):
+    torch = _torch()
+    if ws is not None:
+        return ws
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def hessian_accumulate(H, X, ws=None, stream=None):
+    """H += 2 X^T X for X [n_tok, d] (rows may be strided); H [d, d] float32."""
+    d = H.shape[0]
+    assert H.is_contiguous() and H.shape == (d, d) and X.dim() == 2 and X.shape[1] == d
+    assert X.stride(1) == 1
+    xd = _dtype_code(X)
+    n_tok = X.shape[0]
+    need = lib().gptq_hessian_workspace_size(d, n_tok, xd)
+    ws = _workspace(need, H.device, ws)
+    _check(lib().gptq_hessian_accumulate(H.data_ptr(), d, X.data_ptr(), xd, n_tok, X.stride(0),
+                                         ws.data_ptr(), ws.numel() * ws.element_size(),
+                                         _stream_handle(stream)))
+    return H
+
+
+def prepare_hinv(H, G=None, damp_frac=0.01, ws=None, check=True, stream=None):
+    """G = Cholesky((H + lambda I)^-1)^T.  check=True waits and raises on a bad pivot."""
+    torch = _torch()
+    d = H.shape[0]
+    assert H.is_contiguous() and H.dtype == torch.float32
+    if G is None:
+        G = torch.empty_like(H)
+    ws = _workspace(lib().gptq_prepare_workspace_size(d), H.device, ws)
+    info = _i64(0)
+    _check(lib().gptq_prepare_hinv(H.data_ptr(), G.data_ptr(), d, float(damp_frac), ws.data_ptr(),
+                                   ws.numel() * ws.element_size(),
+                                   ctypes.byref(info) if check else None, _stream_handle(stream)))
+    return G
+
+
+def quantize_layer(W, G, spec: Spec, qweight=None, scales=None, zeros=None, err_sq=True,
+                   ws=None, stream=None):
+    """Returns (qweight int32 view of the uint32 words, scales, zeros uint8, err_sq_rows)."""
+    torch = _torch()
+    d_row, d_col = W.shape
+    assert W.is_contiguous() and G.is_contiguous() and G.shape == (d_col, d_col)
+    g = d_col if spec.group == 0 else spec.group
+    ng = d_col // g
+    dev = W.device
+    if qweight is None:
+        qweight = torch.empty((d_row, d_col * spec.bits // 32), dtype=torch.int32, device=dev)
+    if scales is None:
+        scales = torch.empty((d_row, ng), dtype=torch.float32, device=dev)
+    if zeros is None:
+        zeros = torch.empty((d_row, ng), dtype=torch.uint8, device=dev)
+    esq = torch.empty(d_row, dtype=torch.float64, device=dev) if err_sq is True else err_sq
+    need = lib().gptq_quantize_workspace_size(d_row, d_col, ctypes.byref(spec))
+    ws = _workspace(need, dev, ws)
+    _check(lib().gptq_quantize_layer(W.data_ptr(), _dtype_code(W), d_row, d_col, G.data_ptr(),
+                                     ctypes.byref(spec), qweight.data_ptr(), scales.data_ptr(),
+                                     zeros.data_ptr(), esq.data_ptr() if esq is not None else None,
+                                     ws.data_ptr(), ws.numel() * ws.element_size(),
+                                     _stream_handle(stream)))
+    return qweight, scales, zeros, esq
+
+
+def dequant_check(qweight, scales, zeros, W, H, spec: Spec, want_w_hat=False, ws=None, stream=None):
+    """Returns (loss float64[1], row_loss float64[d_row], W_hat or None, off_grid int64[1])."""
+    torch = _torch()
+    d_row, d_col = W.shape
+    dev = W.device
+    loss = torch.empty(1, dtype=torch.float64, device=dev)
+    row_loss = torch.empty(d_row, dtype=torch.float64, device=dev)
+    off = torch.empty(1, dtype=torch.int64, device=dev)
+    w_hat = torch.empty((d_row, d_col), dtype=torch.float32, device=dev) if want_w_hat else None
+    ws = _workspace(lib().gptq_check_workspace_size(d_row, d_col), dev, ws)
+    _check(lib().gptq_dequant_check(qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                                    W.data_ptr(), _dtype_code(W), H.data_ptr(), d_row, d_col,
+                                    ctypes.byref(spec), loss.data_ptr(), row_loss.data_ptr(),
+                                    w_hat.data_ptr() if w_hat is not None else None,
+                                    off.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                    _stream_handle(stream)))
+    return loss, row_loss, w_hat, off
+
+
+def profile_enable(on=True):
+    _check(lib().gptq_profile_enable(int(bool(on))))
+
+
+def profile_reset():
+    _check(lib().gptq_profile_reset())
+
+
+def profile_read(kernel: str):
+    n = _i64(0)
+    ms = ctypes.c_double(0.0)
+    _check(lib().gptq_profile_read(kernel.encode(), ctypes.byref(n), ctypes.byref(ms)))
+    return int(n.value), float(ms.value)

@@ -1,0 +1,119 @@
+"""The C ABI on a host without a GPU: the library loads, exports every function that
+include/gptq.h declares, and rejects bad arguments before any HIP call."""
+import ctypes
+
+import pytest
+
+from post_weight_quantization_24_amd import gptq as G
+
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails or returns first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return G.lib()
+
+
+def test_exports_every_header_function(lib):
+    names = G.header_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(G._SIGS)
+
+
+def test_version_and_strings(lib):
+    assert "gfx950" in G.version()
+    for code in (G.OK, G.EINVAL, G.ENOTSPD, G.EHIP, G.ENOWS):
+        assert lib.gptq_strerror(code)
+    assert lib.gptq_last_error() == b""
+
+
+def test_hessian_validation(lib):
+    f = lib.gptq_hessian_accumulate
+    assert f(FAKE, 0, FAKE, 0, 10, 8, FAKE, 1 << 30, None) == G.EINVAL
+    assert b"d out of range" in lib.gptq_last_error()
+    assert f(FAKE, 16, FAKE, 5, 10, 16, FAKE, 1 << 30, None) == G.EINVAL
+    assert f(None, 16, FAKE, 0, 10, 16, FAKE, 1 << 30, None) == G.EINVAL
+    assert f(FAKE, 16, None, 0, 10, 16, FAKE, 1 << 30, None) == G.EINVAL
+    assert f(FAKE, 16, FAKE, 0, -1, 16, FAKE, 1 << 30, None) == G.EINVAL
+    assert f(FAKE, 16, FAKE, 0, 10, 8, FAKE, 1 << 30, None) == G.EINVAL          # ldx < d
+    assert f(FAKE, 16, ctypes.c_void_p(0x10002), 0, 10, 16, FAKE, 1 << 30, None) == G.EINVAL
+    assert f(FAKE, 12, FAKE, 0, 10, 12, FAKE, 1 << 30, None) == G.EINVAL         # row not 16B
+    assert f(FAKE, 16, FAKE, 0, 10, 16, FAKE, 16, None) == G.ENOWS
+    assert f(FAKE, 16, FAKE, 0, 10, 16, None, 1 << 30, None) == G.ENOWS
+    assert f(FAKE, 16, FAKE, 0, 0, 16, None, 0, None) == G.OK                    # empty chunk
+
+
+def test_prepare_validation(lib):
+    f = lib.gptq_prepare_hinv
+    ws = lib.gptq_prepare_workspace_size(64)
+    assert ws >= 64 * 64 // 4 * 4
+    assert f(FAKE, FAKE, 0, 0.01, FAKE, ws, None, None) == G.EINVAL
+    assert f(None, FAKE, 64, 0.01, FAKE, ws, None, None) == G.EINVAL
+    assert f(FAKE, FAKE, 64, -0.5, FAKE, ws, None, None) == G.EINVAL
+    assert f(FAKE, FAKE, 64, float("nan"), FAKE, ws, None, None) == G.EINVAL
+    assert f(FAKE, FAKE, 64, 0.01, FAKE, ws - 1, None, None) == G.ENOWS
+
+
+def _spec(**kw):
+    base = dict(bits=4, group=128, sym=0, block=128, damp_frac=0.01)
+    base.update(kw)
+    return G.Spec(**base)
+
+
+@pytest.mark.parametrize("kw,d_col,msg", [
+    (dict(bits=5), 256, b"bits"),
+    (dict(block=96), 256, b"block"),
+    (dict(group=8), 256, b"multiple of 16"),
+    (dict(group=96), 256, b"does not divide"),
+    (dict(group=48, block=32), 480, b"nest"),
+    (dict(sym=2), 256, b"sym"),
+    (dict(), 250, b"multiple of 32"),
+])
+def test_quantize_validation(lib, kw, d_col, msg):
+    spec = _spec(**kw)
+    rc = lib.gptq_quantize_layer(FAKE, 0, 64, d_col, FAKE, ctypes.byref(spec), FAKE, FAKE, FAKE,
+                                 None, FAKE, 1 << 40, None)
+    assert rc == G.EINVAL
+    assert msg in lib.gptq_last_error()
+    assert lib.gptq_quantize_workspace_size(64, d_col, ctypes.byref(spec)) == 0
+
+
+def test_quantize_workspace_and_nulls(lib):
+    spec = _spec(group=0, block=64)
+    need = lib.gptq_quantize_workspace_size(300, 512, ctypes.byref(spec))
+    assert need >= 300 * 512 * 4 + 300 * 64 * 4
+    args = [FAKE, 1, 300, 512, FAKE, ctypes.byref(spec), FAKE, FAKE, FAKE, None, FAKE, need - 1, None]
+    assert lib.gptq_quantize_layer(*args) == G.ENOWS
+    args[4] = None
+    args[11] = need
+    assert lib.gptq_quantize_layer(*args) == G.EINVAL
+    args = [FAKE, 7, 300, 512, FAKE, ctypes.byref(spec), FAKE, FAKE, FAKE, None, FAKE, need, None]
+    assert lib.gptq_quantize_layer(*args) == G.EINVAL
+
+
+def test_check_validation(lib):
+    spec = _spec()
+    need = lib.gptq_check_workspace_size(64, 256)
+    assert need >= 2 * 64 * 256 * 4
+    f = lib.gptq_dequant_check
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, FAKE, 64, 256, ctypes.byref(spec), None, None, None, FAKE,
+             FAKE, need, None) == G.EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, FAKE, 64, 256, ctypes.byref(spec), FAKE, None, None, FAKE,
+             FAKE, need - 1, None) == G.ENOWS
+
+
+def test_hessian_workspace_plan(lib):
+    # 4096 channels -> 136 lower tiles of 256x256; split over tokens into partial tiles
+    ws = lib.gptq_hessian_workspace_size(4096, 262144, 0)
+    tile = 256 * 256 * 4
+    assert ws % (136 * tile) == 0 and 1 <= ws // (136 * tile) <= 64
+    assert lib.gptq_hessian_workspace_size(300, 1000, 1) == 3 * tile   # 2x2 blocks, 1 split
+    assert lib.gptq_hessian_workspace_size(0, 10, 0) == 0
+
+
+def test_profile_calls_without_gpu(lib):
+    G.profile_enable(False)
+    G.profile_reset()
+    assert G.profile_read("hessian_mfma") == (0, 0.0)
