@@ -124,7 +124,7 @@ def main():
     H = torch.empty((d_col, d_col), dtype=torch.float32, device=dev)
     Gm = torch.empty_like(H)
     L = G.lib()
-    ws_h = torch.empty(max(L.gptq_hessian_workspace_size(d_col, n_tok, G._dtype_code(Xd)), 256),
+    ws_h = torch.empty(max(L.gptq_hessian_workspace_size(d_col, n_tok, d_col, G._dtype_code(Xd)), 256),
                        dtype=torch.uint8, device=dev)
     ws_p = torch.empty(L.gptq_prepare_workspace_size(d_col), dtype=torch.uint8, device=dev)
     import ctypes

@@ -93,8 +93,10 @@ const char* gptq_last_error(void);
  *          (elements) >= d.  x_dtype GPTQ_F16 (products exact, float32 accumulation)
  *          or GPTQ_F32.  X and ldx * element size must be 16-byte aligned.
  *   n_tok  >= 0; 0 is a no-op.
+ *   ws     workspace of gptq_hessian_workspace_size(d, n_tok, ldx, x_dtype) bytes (the
+ *          float32 partial tiles of the token ranges processed in parallel).
  * Errors: GPTQ_EINVAL, GPTQ_ENOWS, GPTQ_EHIP. */
-size_t gptq_hessian_workspace_size(int64_t d, int64_t n_tok, int x_dtype);
+size_t gptq_hessian_workspace_size(int64_t d, int64_t n_tok, int64_t ldx, int x_dtype);
 int gptq_hessian_accumulate(float* H, int64_t d, const void* X, int x_dtype, int64_t n_tok,
                             int64_t ldx, void* ws, size_t ws_bytes, void* stream);
 

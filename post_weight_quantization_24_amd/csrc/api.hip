@@ -137,9 +137,9 @@ const char* gptq_strerror(int code) {
 const char* gptq_last_error(void) { return g_last_error.c_str(); }
 
 // ---------------------------------------------------------------- Hessian
-size_t gptq_hessian_workspace_size(int64_t d, int64_t n_tok, int x_dtype) {
-  if (d < 1 || n_tok < 1 || (x_dtype != GPTQ_F16 && x_dtype != GPTQ_F32)) return 0;
-  return gptq::hessian_plan(d, n_tok, x_dtype).ws_bytes;
+size_t gptq_hessian_workspace_size(int64_t d, int64_t n_tok, int64_t ldx, int x_dtype) {
+  if (d < 1 || n_tok < 1 || ldx < d || (x_dtype != GPTQ_F16 && x_dtype != GPTQ_F32)) return 0;
+  return gptq::hessian_plan(d, n_tok, ldx, x_dtype).ws_bytes;
 }
 
 int gptq_hessian_accumulate(float* H, int64_t d, const void* X, int x_dtype, int64_t n_tok,
@@ -155,7 +155,7 @@ int gptq_hessian_accumulate(float* H, int64_t d, const void* X, int x_dtype, int
   const size_t elt = x_dtype == GPTQ_F16 ? 2 : 4;
   if (!aligned(X, 16) || (ldx * (int64_t)elt) % 16 != 0)
     return fail(GPTQ_EINVAL, "X and its rows must be 16-byte aligned");
-  const gptq::HessPlan p = gptq::hessian_plan(d, n_tok, x_dtype);
+  const gptq::HessPlan p = gptq::hessian_plan(d, n_tok, ldx, x_dtype);
   if (!ws || ws_bytes < p.ws_bytes)
     return fail(GPTQ_ENOWS, "workspace of %zu bytes needed", p.ws_bytes);
   if (!aligned(ws, 16)) return fail(GPTQ_EINVAL, "workspace must be 16-byte aligned");

@@ -29,7 +29,7 @@ struct HessPlan {
   int64_t tok_per_split;
   size_t ws_bytes;
 };
-HessPlan hessian_plan(int64_t d, int64_t n_tok, int x_dtype);
+HessPlan hessian_plan(int64_t d, int64_t n_tok, int64_t ldx, int x_dtype);
 hipError_t hessian_launch(const HessPlan& p, float* H, const void* X, int x_dtype, int64_t ldx,
                           void* ws, hipStream_t stream);
 

@@ -9,11 +9,7 @@
 //     fixed order (deterministic, no float atomics), scales by 2, adds into H and writes
 //     both triangles.
 //   * f16 inputs: v_mfma_f32_32x32x16_f16 (products of f16 values are exact in the f32
-//     accumulator).  X rows are channel-contiguous, but MFMA operands need 8 consecutive
-//     tokens of one channel per lane, so each thread loads an 8-token x 8-channel block
-//     (eight 16-byte row loads), transposes it in registers and writes eight 16-byte
-//     channel runs to LDS, stored [channel][token] with a 16-byte pad per channel row so
-//     that both the stores and the MFMA operand reads are free of bank conflicts.
+//     accumulator), fed by direct global-to-LDS copies and transposed LDS reads (below).
 //   * f32 inputs (small layers): a VALU kernel with the same partial-tile output.
 
 #include "gptq_internal.h"
@@ -23,8 +19,6 @@ namespace gptq {
 namespace {
 
 constexpr int TILE = 256;         // H tile edge
-constexpr int BK = 64;            // tokens per LDS stage
-constexpr int LDS_ROW = BK + 8;   // halfs per channel row in LDS (16-byte pad)
 
 __device__ __forceinline__ void tile_coords(int tile, int& ti, int& tj) {
   // tile = ti*(ti+1)/2 + tj with 0 <= tj <= ti
@@ -35,144 +29,172 @@ __device__ __forceinline__ void tile_coords(int tile, int& ti, int& tj) {
   tj = tile - t * (t + 1) / 2;
 }
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// ---------------------------------------------------------------------------------
+// f16 inputs, direct-to-LDS pipeline (the launch path).
+//
+// Each stage holds 32 tokens x 256 channels of the two channel blocks, copied from X by
+// buffer loads that write LDS directly (the buffer covers exactly the workgroup's token
+// range, so reads past its end return zeros: no masking for ragged token counts).  LDS
+// keeps X's token-major layout; the MFMA operands (8 consecutive tokens of one channel per
+// lane) come from transposed LDS reads: within each 16-lane group of ds_read_b64_tr_b16,
+// lane i receives element i%4 of the 8-byte pieces addressed by lanes 4m + i/4 (m = 0..3),
+// so lane j pointing at (token k0 + j/4, channels c0 + 4(j%4)..) hands lane i channel c0+i
+// at tokens k0..k0+3.  The 16-byte slots of a token row are XOR-swizzled by 4*(row % 4)
+// so that the four rows such a group touches fall on distinct banks.
+// Loads run three stages ahead of the MFMAs; each stage is a separate LDS array so that
+// waiting for one stage never waits for the loads of the later ones.
+constexpr int V2_BK = 32;                                 // tokens per stage
+constexpr int V2_STAGE_HALFS = V2_BK * TILE;              // 8192 halfs = 16 KB per operand
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) short4v lds_s4;
 
-// One 8x8 f16 block: rows r = tokens, 4 dwords each holding channels (2p, 2p+1).
-// Output o[c][p] holds tokens (2p, 2p+1) of channel c.
-__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+__device__ __forceinline__ int v2_slot(int row, int chunk) { return chunk ^ (4 * (row & 3)); }
+
+typedef uint32_t rsrc_t __attribute__((ext_vector_type(4)));
+
+// One wave-wide 1 KB copy global -> LDS: lane l's 16 bytes at buffer offset voff land at
+// lds_base + 16 l.  Written as asm so that the compiler's wait insertion does not treat
+// every later LDS read as dependent on it (it would drain the whole pipeline); the
+// explicit vmcnt waits before each stage barrier order the copies.  No register output.
+__device__ __forceinline__ void dma16(rsrc_t rsrc, uint32_t lds_base, int voff) {
+  __asm__ volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                   :
+                   : "v"(voff), "s"(rsrc), "s"(lds_base)
+                   : "memory", "m0");
+}
+
+// Issue this wave's share of one operand's stage: 16 wave-wide 1 KB copies per operand,
+// 4 per wave; copy q covers token rows 2q, 2q+1 of the stage.
+__device__ __forceinline__ void v2_load_operand(rsrc_t rsrc, short* dst, int tok_in_range,
+                                                int64_t ldx, int64_t ch0, int wave, int lane) {
+  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)dst);
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      uint32_t x = in[2 * p][m], y = in[2 * p + 1][m];
-      out[2 * m][p] = (x & 0xffffu) | (y << 16);
-      out[2 * m + 1][p] = (x >> 16) | (y & 0xffff0000u);
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int q = wave * 4 + i;
+    const int row = 2 * q + (lane >> 5);
+    const int slot = lane & 31;
+    const int chunk = v2_slot(row, slot);            // XOR is an involution
+    const int voff = (int)(((int64_t)(tok_in_range + row) * ldx + ch0 + 8 * chunk) * 2);
+    dma16(rsrc, __builtin_amdgcn_readfirstlane(lds0 + q * 1024), voff);
   }
 }
 
-template <int WAVES_M, int WAVES_N, int TM, int TN>
-struct HessCfg {
-  static constexpr int NWAVES = WAVES_M * WAVES_N;
-  static constexpr int NTHREADS = NWAVES * 64;
-  static_assert(WAVES_M * TM * 32 == TILE && WAVES_N * TN * 32 == TILE, "tile shape");
-  // micro-blocks (8 tokens x 8 channels) per operand per stage: (TILE/8) * (BK/8)
-  static constexpr int MB_PER_OPERAND = (TILE / 8) * (BK / 8);
-  static constexpr int MB_PER_THREAD = 2 * MB_PER_OPERAND / NTHREADS;
-  static_assert(MB_PER_THREAD * NTHREADS == 2 * MB_PER_OPERAND, "loader shape");
-};
+// Operand fragment for one 32x32x16 MFMA: channels c_base..+31, tokens k_sub..+15 of a stage.
+__device__ __forceinline__ half8 v2_frag(const short* stage, int c_base, int k_sub, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int ch = c_base + 16 * (g & 1) + 4 * (j & 3);
+  const int chunk = ch >> 3, half_off = (ch & 7);   // 0 or 4 halfs into the chunk
+  const int r0 = k_sub + 8 * (g >> 1) + (j >> 2);
+  const int r1 = r0 + 4;
+  const short* p0 = stage + r0 * TILE + v2_slot(r0, chunk) * 8 + half_off;
+  const short* p1 = stage + r1 * TILE + v2_slot(r1, chunk) * 8 + half_off;
+  const short4v a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)p0);
+  const short4v b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)p1);
+  const short4v c8[2] = {a, b};
+  half8 out;
+  __builtin_memcpy(&out, c8, sizeof(out));
+  return out;
+}
 
-template <int WAVES_M, int WAVES_N, int TM, int TN>
-__global__ void __launch_bounds__(WAVES_M* WAVES_N * 64, 1)
-hess_f16_mfma(const _Float16* __restrict__ X, int64_t ldx, int64_t d, int64_t n_tok,
-              int64_t tok_per_split, int tiles, float* __restrict__ part) {
-  using C = HessCfg<WAVES_M, WAVES_N, TM, TN>;
-  __shared__ __attribute__((aligned(16))) _Float16 lds[2 * TILE * LDS_ROW];
-  _Float16* lds_a = lds;
-  _Float16* lds_b = lds + TILE * LDS_ROW;
+// vmcnt wait with compile-time count (gfx9 encoding; expcnt and lgkmcnt left unconstrained)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Workgroup barrier without the memory fence of __syncthreads (whose release half would
+// drain every outstanding load, including the stages meant to stay in flight).  The caller
+// has waited for the loads it needs; lgkmcnt(0) retires this wave's LDS reads first.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt((15 & 15) | (3 << 14) | (7 << 4) | (0 << 8));
+  __builtin_amdgcn_s_barrier();
+}
+
+__global__ void __launch_bounds__(256, 1)
+hess_f16_lds(const _Float16* __restrict__ X, int64_t ldx, int64_t d, int64_t n_tok,
+             int64_t tok_per_split, int tiles, float* __restrict__ part) {
+  // 4 stages x {A, B} x 32 tokens x 256 channels
+  __shared__ __attribute__((aligned(16))) short lds[4 * 2 * V2_STAGE_HALFS];
 
   const int tile = blockIdx.x % tiles;
   const int split = blockIdx.x / tiles;
   int ti, tj;
   tile_coords(tile, ti, tj);
-  const int64_t ca0 = (int64_t)ti * TILE;  // channel block of H rows
-  const int64_t cb0 = (int64_t)tj * TILE;  // channel block of H cols
+  const bool diag = ti == tj;
+  const int64_t ca0 = (int64_t)ti * TILE, cb0 = (int64_t)tj * TILE;
   const int64_t t_begin = (int64_t)split * tok_per_split;
   int64_t t_end = t_begin + tok_per_split;
   if (t_end > n_tok) t_end = n_tok;
+  const int64_t n_here = t_end > t_begin ? t_end - t_begin : 0;
+  const int nsteps = (int)((n_here + V2_BK - 1) / V2_BK);
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WAVES_N;
-  const int wn = wave % WAVES_N;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (LDS base in M0)
+  const int wm = wave >> 1, wn = wave & 1;
+  // buffer over exactly this workgroup's tokens; bytes beyond it read as zero
+  // (built from readfirstlane'd values so that it lives in scalar registers)
+  const uint64_t base = reinterpret_cast<uint64_t>(X + (n_here ? t_begin : 0) * ldx);
+  const uint32_t base_lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t base_hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  const int nbytes = __builtin_amdgcn_readfirstlane((int)(n_here * ldx * 2));
+  // buffer descriptor: base, stride 0, size in bytes, raw 32-bit data format
+  const rsrc_t rsrc = {base_lo, base_hi & 0xffffu, (uint32_t)nbytes, 0x00020000u};
 
-  floatx16 acc[TM][TN];
+  floatx16 acc[4][4];
 #pragma unroll
-  for (int a = 0; a < TM; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < TN; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-  // loader: micro-block index mb = tid + i*NTHREADS over [A blocks | B blocks];
-  // within an operand: tb = mb % 8 (token block), cbk = mb / 8 (channel block).
-  u32x4 stage[C::MB_PER_THREAD][8];
-
-  auto load_stage = [&](int64_t k0) {
-#pragma unroll
-    for (int i = 0; i < C::MB_PER_THREAD; ++i) {
-      const int mb = tid + i * C::NTHREADS;
-      const int op = mb / C::MB_PER_OPERAND;
-      const int r = mb % C::MB_PER_OPERAND;
-      const int tb = r % 8;
-      const int cbk = r / 8;
-      const int64_t ch = (op ? cb0 : ca0) + cbk * 8;
-      const bool ch_ok = ch < d;
-#pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const int64_t t = k0 + tb * 8 + rr;
-        if (ch_ok && t < t_end) {
-          stage[i][rr] = *reinterpret_cast<const u32x4*>(X + t * ldx + ch);
-        } else {
-          stage[i][rr] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-  };
-  auto store_stage = [&]() {
-#pragma unroll
-    for (int i = 0; i < C::MB_PER_THREAD; ++i) {
-      const int mb = tid + i * C::NTHREADS;
-      const int op = mb / C::MB_PER_OPERAND;
-      const int r = mb % C::MB_PER_OPERAND;
-      const int tb = r % 8;
-      const int cbk = r / 8;
-      u32x4 tr[8];
-      transpose8x8(stage[i], tr);
-      _Float16* base = (op ? lds_b : lds_a) + (cbk * 8) * LDS_ROW + tb * 8;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) *reinterpret_cast<u32x4*>(base + c * LDS_ROW) = tr[c];
-    }
+  auto stage_a = [&](int st) { return lds + (st & 3) * 2 * V2_STAGE_HALFS; };
+  auto issue = [&](int st) {
+    short* a_dst = stage_a(st);
+    v2_load_operand(rsrc, a_dst, st * V2_BK, ldx, ca0, wave, lane);
+    if (!diag) v2_load_operand(rsrc, a_dst + V2_STAGE_HALFS, st * V2_BK, ldx, cb0, wave, lane);
   };
 
-  int64_t k0 = t_begin;
-  if (k0 < t_end) load_stage(k0);
-  for (; k0 < t_end; k0 += BK) {
-    __syncthreads();  // previous stage's LDS reads are done
-    store_stage();
-    __syncthreads();
-    if (k0 + BK < t_end) load_stage(k0 + BK);  // prefetch overlaps the MFMAs below
+  if (nsteps > 0) issue(0);
+  if (nsteps > 1) issue(1);
+  if (nsteps > 2) issue(2);
+  for (int s = 0; s < nsteps; ++s) {
+    // stage s has landed once at most `later` stages issued after it are pending
+    // (copies retire in order; 4 per operand per wave and stage)
+    const int later = nsteps - 1 - s < 2 ? nsteps - 1 - s : 2;
+    if (diag) {
+      if (later == 2) wait_vmcnt<8>(); else if (later == 1) wait_vmcnt<4>(); else wait_vmcnt<0>();
+    } else {
+      if (later == 2) wait_vmcnt<16>(); else if (later == 1) wait_vmcnt<8>(); else wait_vmcnt<0>();
+    }
+    stage_barrier();
+    if (s + 3 < nsteps) issue(s + 3);      // into the buffer read in iteration s - 1
+    const short* sa = stage_a(s);
+    const short* sb = diag ? sa : sa + V2_STAGE_HALFS;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      half8 af[TM], bf[TN];
-      const int koff = kk * 16 + 8 * (lane >> 5);
+    for (int kk = 0; kk < V2_BK / 16; ++kk) {
+      half8 af[4], bf[4];
 #pragma unroll
-      for (int a = 0; a < TM; ++a)
-        af[a] = *reinterpret_cast<const half8*>(
-            lds_a + (wm * TM * 32 + a * 32 + (lane & 31)) * LDS_ROW + koff);
+      for (int a = 0; a < 4; ++a) af[a] = v2_frag(sa, wm * 128 + a * 32, kk * 16, lane);
 #pragma unroll
-      for (int b = 0; b < TN; ++b)
-        bf[b] = *reinterpret_cast<const half8*>(
-            lds_b + (wn * TN * 32 + b * 32 + (lane & 31)) * LDS_ROW + koff);
+      for (int b = 0; b < 4; ++b) bf[b] = v2_frag(sb, wn * 128 + b * 32, kk * 16, lane);
 #pragma unroll
-      for (int a = 0; a < TM; ++a)
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < TN; ++b)
+        for (int b = 0; b < 4; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
     }
   }
 
-  // partial tile [TILE][TILE] for (split, tile)
   float* out = part + ((int64_t)split * tiles + tile) * (int64_t)TILE * TILE;
 #pragma unroll
-  for (int a = 0; a < TM; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < TN; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = wm * TM * 32 + a * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int col = wn * TN * 32 + b * 32 + (lane & 31);
+        const int row = wm * 128 + a * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int col = wn * 128 + b * 32 + (lane & 31);
         out[row * TILE + col] = acc[a][b][r];
       }
 }
@@ -262,10 +284,11 @@ hess_reduce(const float* __restrict__ part, int splits, int tiles, int64_t d,
 
 }  // namespace
 
-HessPlan hessian_plan(int64_t d, int64_t n_tok, int x_dtype) {
+HessPlan hessian_plan(int64_t d, int64_t n_tok, int64_t ldx, int x_dtype) {
   HessPlan p{};
   p.d = d;
   p.n_tok = n_tok;
+  if (ldx < d) ldx = d;
   const int64_t nb = ceil_div(d, TILE);
   p.tiles = (int)(nb * (nb + 1) / 2);
   // Enough workgroups to fill 256 CUs with a short tail, each split >= 2048 tokens.
@@ -274,7 +297,11 @@ HessPlan hessian_plan(int64_t d, int64_t n_tok, int x_dtype) {
   int best = 1;
   double best_cost = 1e30;
   const int64_t max_split = n_tok / min_tok > 1 ? n_tok / min_tok : 1;
-  for (int64_t s = 1; s <= max_split && s <= 64; ++s) {
+  // one split's rows must stay below 2^30 bytes (32-bit buffer offsets)
+  const int64_t elt = x_dtype == 0 ? 2 : 4;
+  const int64_t min_split = ceil_div(n_tok * ldx * elt, (int64_t)1 << 30);
+  for (int64_t s = min_split; s <= max_split || s == min_split; ++s) {
+    if (s > 64 && s > min_split) break;
     const int64_t wgs = p.tiles * s * (x_dtype == 0 ? 1 : 16);
     const double rounds = (double)ceil_div(wgs, cus);
     // time ~ rounds * work per workgroup (1/s), plus partial-tile traffic per split
@@ -286,8 +313,8 @@ HessPlan hessian_plan(int64_t d, int64_t n_tok, int x_dtype) {
   }
   p.splits = best;
   int64_t tps = ceil_div(n_tok, best);
-  tps = ceil_div(tps, BK) * BK;
-  p.tok_per_split = tps > 0 ? tps : BK;
+  tps = ceil_div(tps, 64) * 64;
+  p.tok_per_split = tps > 0 ? tps : 64;
   p.ws_bytes = (size_t)p.splits * p.tiles * TILE * TILE * sizeof(float);
   return p;
 }
@@ -298,9 +325,9 @@ hipError_t hessian_launch(const HessPlan& p, float* H, const void* X, int x_dtyp
   {
     ProfScope ps("hessian_mfma", stream);
     if (x_dtype == 0) {
-      hipLaunchKernelGGL((hess_f16_mfma<2, 2, 4, 4>), dim3(p.tiles * p.splits), dim3(256), 0,
-                         stream, static_cast<const _Float16*>(X), ldx, p.d, p.n_tok,
-                         p.tok_per_split, p.tiles, part);
+      hipLaunchKernelGGL(hess_f16_lds, dim3(p.tiles * p.splits), dim3(256), 0, stream,
+                         static_cast<const _Float16*>(X), ldx, p.d, p.n_tok, p.tok_per_split,
+                         p.tiles, part);
     } else {
       hipLaunchKernelGGL(hess_f32_valu, dim3(p.tiles * p.splits * 16), dim3(256), 0, stream,
                          static_cast<const float*>(X), ldx, p.d, p.n_tok, p.tok_per_split,

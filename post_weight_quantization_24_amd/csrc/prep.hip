@@ -11,7 +11,7 @@
 //     G11 = factor(A11)                     (recursion)
 //     G12 = -G11 (P G22) = -G11 A12
 // All products run on the fp32 MFMA GEMM; blocks of at most 128 are factored and
-// inverted by one workgroup in LDS.  Everything happens in the upper triangle of G;
+// inverted by one workgroup in registers.  Everything happens in the upper triangle of G;
 // the strictly lower triangle is zeroed at the end.
 
 #include <climits>
@@ -23,7 +23,6 @@ namespace gptq {
 namespace {
 
 constexpr int NB = 128;           // leaf size
-constexpr int LEAF_LD = NB + 1;   // LDS row stride
 
 struct PrepWs {
   double* lambda;
@@ -92,63 +91,132 @@ dim3 rows_grid(int64_t rows, int64_t cols) {
 }
 
 // Factor the n x n diagonal block at (off, off) as U U^T (U upper) and overwrite its
-// upper triangle with G = U^-1.  One workgroup; 16 x 16 threads stride over the block.
+// upper triangle with G = U^-1.  One workgroup of 16 x 16 threads; thread (tx, ty) keeps
+// the 8 x 8 tile at rows 8ty.., cols 8tx.. of the symmetric block in registers.  Each
+// column step publishes one column (and, for the inverse, one row) through
+// double-buffered LDS, so a step costs one barrier plus at most 64 register FMAs.
+template <int KK>
+__device__ __forceinline__ void chol_step(float (&S)[8][8], int k, int tx, int ty, int i0, int j0,
+                                          float (*colbuf)[NB], float* diag, int* bad) {
+  const int b = k & 1;
+  if (tx == (k >> 3)) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) colbuf[b][i0 + r] = S[r][KK];
+  }
+  __syncthreads();
+  const float piv = colbuf[b][k];
+  if (threadIdx.x == 0) {
+    diag[k] = piv;
+    if (!(piv > 0.0f) || !(piv < 3.0e38f)) *bad = k;
+  }
+  if (i0 < k && j0 < k) {
+    const float rp = 1.0f / piv;
+    float ci[8], cj[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) ci[r] = (i0 + r < k) ? colbuf[b][i0 + r] : 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) cj[q] = (j0 + q < k) ? colbuf[b][j0 + q] * rp : 0.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) S[r][q] = fmaf(-ci[r], cj[q], S[r][q]);
+  }
+}
+
+template <int KK>
+__device__ __forceinline__ void inv_step(const float (&U)[8][8], float (&R)[8][8], int k, int tx,
+                                         int ty, int i0, int j0, float (*ucol)[NB],
+                                         float (*rrow)[NB], const float* diag) {
+  const int b = k & 1;
+  if (tx == (k >> 3)) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) ucol[b][i0 + r] = U[r][KK];
+  }
+  if (ty == (k >> 3)) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) rrow[b][j0 + q] = R[KK][q];
+  }
+  __syncthreads();
+  if (i0 < k) {
+    const float ru = 1.0f / diag[k];
+    float uc[8], gk[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) uc[r] = (i0 + r < k) ? ucol[b][i0 + r] : 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) gk[q] = rrow[b][j0 + q] * ru;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) R[r][q] = fmaf(-uc[r], gk[q], R[r][q]);
+  }
+}
+
 __global__ void __launch_bounds__(256)
 leaf_factor_invert(float* __restrict__ A, int64_t ld, int64_t off, int n, int* flag) {
-  extern __shared__ float smem[];
-  float* S = smem;                    // factor, upper triangle
-  float* R = smem + NB * LEAF_LD;     // inverse being built, upper triangle
+  __shared__ float colbuf[2][NB];
+  __shared__ float rowbuf[2][NB];
+  __shared__ float diag[NB];
+  __shared__ int bad;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int i0 = 8 * ty, j0 = 8 * tx;
   float* blk = A + off * ld + off;
+  if (threadIdx.x == 0) bad = -1;
 
-  for (int i = ty; i < n; i += 16)
-    for (int j = tx; j < n; j += 16) {
-      S[i * LEAF_LD + j] = (j >= i) ? blk[i * ld + j] : 0.0f;
-      R[i * LEAF_LD + j] = (i == j) ? 1.0f : 0.0f;
+  float S[8][8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int i = i0 + r, j = j0 + q;
+      S[r][q] = (i < n && j < n) ? (j >= i ? blk[(int64_t)i * ld + j] : blk[(int64_t)j * ld + i])
+                                 : (i == j ? 1.0f : 0.0f);
     }
-  __syncthreads();
 
-  // A = U U^T from the bottom-right corner: outer-product updates with unscaled columns.
-  for (int k = n - 1; k > 0; --k) {
-    const float rp = 1.0f / S[k * LEAF_LD + k];
-    for (int j = tx; j < k; j += 16) {
-      const float sjk = S[j * LEAF_LD + k] * rp;
-      for (int i = ty; i <= j; i += 16) S[i * LEAF_LD + j] -= S[i * LEAF_LD + k] * sjk;
-    }
-    __syncthreads();
-  }
-  // pivots are now final on the diagonal
-  if (threadIdx.x == 0) {
-    for (int k = 0; k < n; ++k) {
-      const float p = S[k * LEAF_LD + k];
-      if (!(p > 0.0f) || !(p < 3.0e38f)) {
-        atomicMin(flag, (int)(off + k) + 1);
-        break;
-      }
-    }
-  }
-  // scale columns: U[k][k] = sqrt(p_k), U[i][k] = S[i][k] / sqrt(p_k)
-  for (int j = tx; j < n; j += 16) {
-    const float u = sqrtf(S[j * LEAF_LD + j]);
-    for (int i = ty; i < j; i += 16) S[i * LEAF_LD + j] /= u;
+  // A = U U^T from the bottom-right corner (outer-product form, columns unscaled).
+  for (int kb = NB / 8 - 1; kb >= 0; --kb) {
+#define GPTQ_CHOL(KK) \
+    if (8 * kb + KK < n) chol_step<KK>(S, 8 * kb + KK, tx, ty, i0, j0, colbuf, diag, &bad);
+    GPTQ_CHOL(7) GPTQ_CHOL(6) GPTQ_CHOL(5) GPTQ_CHOL(4)
+    GPTQ_CHOL(3) GPTQ_CHOL(2) GPTQ_CHOL(1) GPTQ_CHOL(0)
+#undef GPTQ_CHOL
   }
   __syncthreads();
-  for (int j = threadIdx.x; j < n; j += 256) S[j * LEAF_LD + j] = sqrtf(S[j * LEAF_LD + j]);
+  if (threadIdx.x == 0 && bad >= 0) atomicMin(flag, (int)(off + bad) + 1);
+  for (int k = threadIdx.x; k < n; k += 256) diag[k] = sqrtf(diag[k]);
   __syncthreads();
-
-  // U G = I, rows from the bottom: row k of R is final at step k.
-  for (int k = n - 1; k > 0; --k) {
-    const float ru = 1.0f / S[k * LEAF_LD + k];
-    for (int j = k + tx; j < n; j += 16) {
-      const float gkj = R[k * LEAF_LD + j] * ru;
-      for (int i = ty; i < k; i += 16) R[i * LEAF_LD + j] -= S[i * LEAF_LD + k] * gkj;
+  // scale to U: U[i][j] = S[i][j] / sqrt(p_j) above the diagonal, sqrt(p_j) on it
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int i = i0 + r, j = j0 + q;
+      const float dj = j < n ? diag[j] : 1.0f;
+      S[r][q] = i < j ? S[r][q] / dj : (i == j ? dj : 0.0f);
     }
-    __syncthreads();
+
+  // U G = I from the bottom row up; R holds the rows of G not yet divided by U[i][i].
+  float R[8][8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) R[r][q] = (i0 + r == j0 + q) ? 1.0f : 0.0f;
+  for (int kb = NB / 8 - 1; kb >= 0; --kb) {
+#define GPTQ_INV(KK) \
+    if (8 * kb + KK < n) inv_step<KK>(S, R, 8 * kb + KK, tx, ty, i0, j0, colbuf, rowbuf, diag);
+    GPTQ_INV(7) GPTQ_INV(6) GPTQ_INV(5) GPTQ_INV(4)
+    GPTQ_INV(3) GPTQ_INV(2) GPTQ_INV(1) GPTQ_INV(0)
+#undef GPTQ_INV
   }
-  for (int i = ty; i < n; i += 16) {
-    const float ru = 1.0f / S[i * LEAF_LD + i];
-    for (int j = tx; j < n; j += 16)
-      if (j >= i) blk[i * ld + j] = R[i * LEAF_LD + j] * ru;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int i = i0 + r;
+    if (i >= n) continue;
+    const float ru = 1.0f / diag[i];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int j = j0 + q;
+      if (j >= i && j < n) blk[(int64_t)i * ld + j] = R[r][q] * ru;
+    }
   }
 }
 
@@ -164,8 +232,7 @@ hipError_t factor_rec(float* A, int64_t ld, int64_t off, int64_t n, float* tmp, 
   hipError_t e;
   if (n <= NB) {
     ProfScope ps("prep_leaf", s);
-    hipLaunchKernelGGL(leaf_factor_invert, dim3(1), dim3(256), 2 * NB * LEAF_LD * sizeof(float),
-                       s, A, ld, off, (int)n, flag);
+    hipLaunchKernelGGL(leaf_factor_invert, dim3(1), dim3(256), 0, s, A, ld, off, (int)n, flag);
     return hipGetLastError();
   }
   int64_t m = (n / 2) / NB * NB;
@@ -196,8 +263,6 @@ hipError_t factor_rec(float* A, int64_t ld, int64_t off, int64_t n, float* tmp, 
   return copy2d(tmp, r, A12, ld, m, r, s);
 }
 
-bool leaf_attr_done = false;
-
 }  // namespace
 
 size_t prepare_ws_bytes(int64_t d) {
@@ -210,13 +275,6 @@ int* prepare_flag_ptr(void* ws, int64_t d) { return carve(ws, d).flag; }
 hipError_t prepare_launch(const float* H, float* G, int64_t d, float damp_frac, void* ws,
                           hipStream_t stream) {
   hipError_t e;
-  if (!leaf_attr_done) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(leaf_factor_invert),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            2 * NB * LEAF_LD * (int)sizeof(float));
-    if (e != hipSuccess) return e;
-    leaf_attr_done = true;
-  }
   PrepWs w = carve(ws, d);
   {
     ProfScope ps("prep_damp", stream);

@@ -41,7 +41,7 @@ _SIGS = {
     "gptq_version": ([], ctypes.c_char_p),
     "gptq_strerror": ([_int], ctypes.c_char_p),
     "gptq_last_error": ([], ctypes.c_char_p),
-    "gptq_hessian_workspace_size": ([_i64, _i64, _int], _sz),
+    "gptq_hessian_workspace_size": ([_i64, _i64, _i64, _int], _sz),
     "gptq_hessian_accumulate": ([_vp, _i64, _vp, _int, _i64, _i64, _vp, _sz, _vp], _int),
     "gptq_prepare_workspace_size": ([_i64], _sz),
     "gptq_prepare_hinv": ([_vp, _vp, _i64, _f32, _vp, _sz, ctypes.POINTER(_i64), _vp], _int),
@@ -130,7 +130,7 @@ def hessian_accumulate(H, X, ws=None, stream=None):
     assert X.stride(1) == 1
     xd = _dtype_code(X)
     n_tok = X.shape[0]
-    need = lib().gptq_hessian_workspace_size(d, n_tok, xd)
+    need = lib().gptq_hessian_workspace_size(d, n_tok, X.stride(0), xd)
     ws = _workspace(need, H.device, ws)
     _check(lib().gptq_hessian_accumulate(H.data_ptr(), d, X.data_ptr(), xd, n_tok, X.stride(0),
                                          ws.data_ptr(), ws.numel() * ws.element_size(),

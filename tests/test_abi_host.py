@@ -106,11 +106,15 @@ def test_check_validation(lib):
 
 def test_hessian_workspace_plan(lib):
     # 4096 channels -> 136 lower tiles of 256x256; split over tokens into partial tiles
-    ws = lib.gptq_hessian_workspace_size(4096, 262144, 0)
+    ws = lib.gptq_hessian_workspace_size(4096, 262144, 4096, 0)
     tile = 256 * 256 * 4
     assert ws % (136 * tile) == 0 and 1 <= ws // (136 * tile) <= 64
-    assert lib.gptq_hessian_workspace_size(300, 1000, 1) == 3 * tile   # 2x2 blocks, 1 split
-    assert lib.gptq_hessian_workspace_size(0, 10, 0) == 0
+    assert lib.gptq_hessian_workspace_size(300, 1000, 300, 1) == 3 * tile   # 2x2 blocks, 1 split
+    assert lib.gptq_hessian_workspace_size(0, 10, 0, 0) == 0
+    assert lib.gptq_hessian_workspace_size(300, 1000, 200, 1) == 0       # ldx < d
+    # a split's rows stay below 2^30 bytes: 65536 tokens of 28672 channels need >= 4 splits
+    big = lib.gptq_hessian_workspace_size(28672, 65536, 28672, 0)
+    assert big // (112 * 113 // 2 * tile) >= 4
 
 
 def test_profile_calls_without_gpu(lib):
