@@ -25,6 +25,7 @@ struct ProfScope {
 struct HessPlan {
   int64_t d, n_tok;
   int tiles;        // number of lower-triangle 256x256 tiles
+  int padded_tiles; // the same for the block grid padded to a multiple of 4 blocks
   int splits;       // token ranges
   int64_t tok_per_split;
   size_t ws_bytes;

@@ -53,6 +53,44 @@ __device__ __forceinline__ int v2_slot(int row, int chunk) { return chunk ^ (4 *
 
 typedef uint32_t rsrc_t __attribute__((ext_vector_type(4)));
 
+// Work item of a workgroup for the f16 kernel.  Workgroups are dispatched round-robin over
+// the 8 XCDs (id % 8), each with its own L2.  When the split count is a multiple of 8, XCD x
+// owns splits x*S/8 .. (x+1)*S/8 - 1 and runs them one after the other, so that the 32 CUs
+// of an XCD stream the same token range at the same time.  Within a split, lower-triangle
+// tiles are visited by 4 x 4-block super-tiles (row-major over the super-tiles, then over
+// the tiles inside one), so that the tiles in flight on an XCD share few channel blocks.
+// The grid covers the triangle padded to a multiple of 4 blocks; padded tiles exit.
+constexpr int SUPER = 4;
+__device__ __forceinline__ void super_tile_coords(int t, int& i, int& j) {
+  // tiles before super-row S: 16 * S(S-1)/2 (off-diagonal) + 10 * S (diagonal)
+  int S = 0;
+  while (8 * (S + 1) * S + 10 * (S + 1) <= t) ++S;
+  int r = t - (8 * S * (S - 1) + 10 * S);
+  if (r < SUPER * SUPER * S) {
+    i = SUPER * S + (r % (SUPER * SUPER)) / SUPER;
+    j = SUPER * (r / (SUPER * SUPER)) + r % SUPER;
+  } else {
+    r -= SUPER * SUPER * S;                       // 0..9 inside the diagonal super-tile
+    int a = 0;
+    while ((a + 1) * (a + 2) / 2 <= r) ++a;
+    i = SUPER * S + a;
+    j = SUPER * S + (r - a * (a + 1) / 2);
+  }
+}
+__device__ __forceinline__ void hess_work(int id, int padded_tiles, int splits, int& split,
+                                          int& ti, int& tj) {
+  int t;
+  if (splits % 8 == 0) {
+    const int xcd = id % 8, k = id / 8;
+    split = xcd * (splits / 8) + k / padded_tiles;
+    t = k % padded_tiles;
+  } else {
+    split = id / padded_tiles;
+    t = id % padded_tiles;
+  }
+  super_tile_coords(t, ti, tj);
+}
+
 // One wave-wide 1 KB copy global -> LDS: lane l's 16 bytes at buffer offset voff land at
 // lds_base + 16 l.  Written as asm so that the compiler's wait insertion does not treat
 // every later LDS read as dependent on it (it would drain the whole pipeline); the
@@ -64,20 +102,16 @@ __device__ __forceinline__ void dma16(rsrc_t rsrc, uint32_t lds_base, int voff) 
                    : "memory", "m0");
 }
 
-// Issue this wave's share of one operand's stage: 16 wave-wide 1 KB copies per operand,
-// 4 per wave; copy q covers token rows 2q, 2q+1 of the stage.
-__device__ __forceinline__ void v2_load_operand(rsrc_t rsrc, short* dst, int tok_in_range,
-                                                int64_t ldx, int64_t ch0, int wave, int lane) {
+// Copy q (0..15) of one operand's stage: a wave-wide 1 KB copy of token rows 2q, 2q+1
+// (16 copies per operand and stage, 4 per wave).
+__device__ __forceinline__ void v2_load_copy(rsrc_t rsrc, short* dst, int tok_in_range, int64_t ldx,
+                                             int64_t ch0, int q, int lane) {
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)dst);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = wave * 4 + i;
-    const int row = 2 * q + (lane >> 5);
-    const int slot = lane & 31;
-    const int chunk = v2_slot(row, slot);            // XOR is an involution
-    const int voff = (int)(((int64_t)(tok_in_range + row) * ldx + ch0 + 8 * chunk) * 2);
-    dma16(rsrc, __builtin_amdgcn_readfirstlane(lds0 + q * 1024), voff);
-  }
+  const int row = 2 * q + (lane >> 5);
+  const int slot = lane & 31;
+  const int chunk = v2_slot(row, slot);            // XOR is an involution
+  const int voff = (int)(((int64_t)(tok_in_range + row) * ldx + ch0 + 8 * chunk) * 2);
+  dma16(rsrc, __builtin_amdgcn_readfirstlane(lds0 + q * 1024), voff);
 }
 
 // Operand fragment for one 32x32x16 MFMA: channels c_base..+31, tokens k_sub..+15 of a stage.
@@ -112,14 +146,15 @@ __device__ __forceinline__ void stage_barrier() {
 
 __global__ void __launch_bounds__(256, 1)
 hess_f16_lds(const _Float16* __restrict__ X, int64_t ldx, int64_t d, int64_t n_tok,
-             int64_t tok_per_split, int tiles, float* __restrict__ part) {
+             int64_t tok_per_split, int tiles, int padded_tiles, int splits,
+             float* __restrict__ part) {
   // 4 stages x {A, B} x 32 tokens x 256 channels
   __shared__ __attribute__((aligned(16))) short lds[4 * 2 * V2_STAGE_HALFS];
 
-  const int tile = blockIdx.x % tiles;
-  const int split = blockIdx.x / tiles;
-  int ti, tj;
-  tile_coords(tile, ti, tj);
+  int split, ti, tj;
+  hess_work(blockIdx.x, padded_tiles, splits, split, ti, tj);
+  if ((int64_t)ti * TILE >= d) return;   // padding of the super-tile grid
+  const int tile = ti * (ti + 1) / 2 + tj;
   const bool diag = ti == tj;
   const int64_t ca0 = (int64_t)ti * TILE, cb0 = (int64_t)tj * TILE;
   const int64_t t_begin = (int64_t)split * tok_per_split;
@@ -149,10 +184,18 @@ hess_f16_lds(const _Float16* __restrict__ X, int64_t ldx, int64_t d, int64_t n_t
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
   auto stage_a = [&](int st) { return lds + (st & 3) * 2 * V2_STAGE_HALFS; };
+  // copy i (0..7) of this wave's share of stage st: 0..3 operand A, 4..7 operand B
+  auto issue_part = [&](int st, int i) {
+    short* dst = stage_a(st) + (i >= 4 ? V2_STAGE_HALFS : 0);
+    v2_load_copy(rsrc, dst, st * V2_BK, ldx, i >= 4 ? cb0 : ca0, wave * 4 + (i & 3), lane);
+  };
   auto issue = [&](int st) {
-    short* a_dst = stage_a(st);
-    v2_load_operand(rsrc, a_dst, st * V2_BK, ldx, ca0, wave, lane);
-    if (!diag) v2_load_operand(rsrc, a_dst + V2_STAGE_HALFS, st * V2_BK, ldx, cb0, wave, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) issue_part(st, i);
+    if (!diag) {
+#pragma unroll
+      for (int i = 4; i < 8; ++i) issue_part(st, i);
+    }
   };
 
   if (nsteps > 0) issue(0);
@@ -168,7 +211,9 @@ hess_f16_lds(const _Float16* __restrict__ X, int64_t ldx, int64_t d, int64_t n_t
       if (later == 2) wait_vmcnt<16>(); else if (later == 1) wait_vmcnt<8>(); else wait_vmcnt<0>();
     }
     stage_barrier();
-    if (s + 3 < nsteps) issue(s + 3);      // into the buffer read in iteration s - 1
+    // stage s + 3 goes into the buffer read in iteration s - 1; its copies are spread
+    // between the MFMAs so that a stalled copy issue does not leave the matrix core idle
+    const bool more = s + 3 < nsteps;
     const short* sa = stage_a(s);
     const short* sb = diag ? sa : sa + V2_STAGE_HALFS;
 #pragma unroll
@@ -179,10 +224,13 @@ hess_f16_lds(const _Float16* __restrict__ X, int64_t ldx, int64_t d, int64_t n_t
 #pragma unroll
       for (int b = 0; b < 4; ++b) bf[b] = v2_frag(sb, wn * 128 + b * 32, kk * 16, lane);
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < 4; ++a) {
 #pragma unroll
         for (int b = 0; b < 4; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
+        const int part = kk * 4 + a;
+        if (more && (part < 4 || !diag)) issue_part(s + 3, part);
+      }
     }
   }
 
@@ -291,6 +339,8 @@ HessPlan hessian_plan(int64_t d, int64_t n_tok, int64_t ldx, int x_dtype) {
   if (ldx < d) ldx = d;
   const int64_t nb = ceil_div(d, TILE);
   p.tiles = (int)(nb * (nb + 1) / 2);
+  const int64_t nbp = ceil_div(nb, 4) * 4;
+  p.padded_tiles = (int)(nbp * (nbp + 1) / 2);
   // Enough workgroups to fill 256 CUs with a short tail, each split >= 2048 tokens.
   const int64_t cus = 256;
   const int64_t min_tok = 2048;
@@ -302,8 +352,12 @@ HessPlan hessian_plan(int64_t d, int64_t n_tok, int64_t ldx, int x_dtype) {
   const int64_t min_split = ceil_div(n_tok * ldx * elt, (int64_t)1 << 30);
   for (int64_t s = min_split; s <= max_split || s == min_split; ++s) {
     if (s > 64 && s > min_split) break;
+    // f16: multiples of 8 splits give each XCD whole token ranges (see hess_work)
+    if (x_dtype == 0 && s >= 8 && s % 8 != 0 && s != min_split) continue;
     const int64_t wgs = p.tiles * s * (x_dtype == 0 ? 1 : 16);
-    const double rounds = (double)ceil_div(wgs, cus);
+    const double rounds = (x_dtype == 0 && s % 8 == 0)
+                              ? (double)ceil_div(p.tiles * (s / 8), cus / 8)
+                              : (double)ceil_div(wgs, cus);
     // time ~ rounds * work per workgroup (1/s), plus partial-tile traffic per split
     const double cost = rounds / (double)s * (x_dtype == 0 ? 1.0 : 1.0 / 16.0) + 0.004 * (double)s;
     if (cost < best_cost - 1e-9) {
@@ -325,9 +379,9 @@ hipError_t hessian_launch(const HessPlan& p, float* H, const void* X, int x_dtyp
   {
     ProfScope ps("hessian_mfma", stream);
     if (x_dtype == 0) {
-      hipLaunchKernelGGL(hess_f16_lds, dim3(p.tiles * p.splits), dim3(256), 0, stream,
+      hipLaunchKernelGGL(hess_f16_lds, dim3(p.padded_tiles * p.splits), dim3(256), 0, stream,
                          static_cast<const _Float16*>(X), ldx, p.d, p.n_tok, p.tok_per_split,
-                         p.tiles, part);
+                         p.tiles, p.padded_tiles, p.splits, part);
     } else {
       hipLaunchKernelGGL(hess_f32_valu, dim3(p.tiles * p.splits * 16), dim3(256), 0, stream,
                          static_cast<const float*>(X), ldx, p.d, p.n_tok, p.tok_per_split,

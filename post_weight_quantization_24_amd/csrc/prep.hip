@@ -111,11 +111,17 @@ __device__ __forceinline__ void chol_step(float (&S)[8][8], int k, int tx, int t
   }
   if (i0 < k && j0 < k) {
     const float rp = 1.0f / piv;
+    // unconditional 16-byte loads (always in bounds), then masks: no branch per element
+    const floatx4* cv = reinterpret_cast<const floatx4*>(colbuf[b]);
+    const floatx4 i_lo = cv[i0 / 4], i_hi = cv[i0 / 4 + 1], j_lo = cv[j0 / 4], j_hi = cv[j0 / 4 + 1];
     float ci[8], cj[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) ci[r] = (i0 + r < k) ? colbuf[b][i0 + r] : 0.0f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) cj[q] = (j0 + q < k) ? colbuf[b][j0 + q] * rp : 0.0f;
+    for (int r = 0; r < 4; ++r) {
+      ci[r] = (i0 + r < k) ? i_lo[r] : 0.0f;
+      ci[r + 4] = (i0 + r + 4 < k) ? i_hi[r] : 0.0f;
+      cj[r] = (j0 + r < k) ? j_lo[r] * rp : 0.0f;
+      cj[r + 4] = (j0 + r + 4 < k) ? j_hi[r] * rp : 0.0f;
+    }
 #pragma unroll
     for (int r = 0; r < 8; ++r)
 #pragma unroll
@@ -139,11 +145,17 @@ __device__ __forceinline__ void inv_step(const float (&U)[8][8], float (&R)[8][8
   __syncthreads();
   if (i0 < k) {
     const float ru = 1.0f / diag[k];
+    const floatx4* uv = reinterpret_cast<const floatx4*>(ucol[b]);
+    const floatx4* rv = reinterpret_cast<const floatx4*>(rrow[b]);
+    const floatx4 u_lo = uv[i0 / 4], u_hi = uv[i0 / 4 + 1], g_lo = rv[j0 / 4], g_hi = rv[j0 / 4 + 1];
     float uc[8], gk[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) uc[r] = (i0 + r < k) ? ucol[b][i0 + r] : 0.0f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) gk[q] = rrow[b][j0 + q] * ru;
+    for (int r = 0; r < 4; ++r) {
+      uc[r] = (i0 + r < k) ? u_lo[r] : 0.0f;
+      uc[r + 4] = (i0 + r + 4 < k) ? u_hi[r] : 0.0f;
+      gk[r] = g_lo[r] * ru;
+      gk[r + 4] = g_hi[r] * ru;
+    }
 #pragma unroll
     for (int r = 0; r < 8; ++r)
 #pragma unroll
@@ -153,8 +165,8 @@ __device__ __forceinline__ void inv_step(const float (&U)[8][8], float (&R)[8][8
 
 __global__ void __launch_bounds__(256)
 leaf_factor_invert(float* __restrict__ A, int64_t ld, int64_t off, int n, int* flag) {
-  __shared__ float colbuf[2][NB];
-  __shared__ float rowbuf[2][NB];
+  __shared__ __attribute__((aligned(16))) float colbuf[2][NB];
+  __shared__ __attribute__((aligned(16))) float rowbuf[2][NB];
   __shared__ float diag[NB];
   __shared__ int bad;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
