@@ -11,7 +11,7 @@
 //     G11 = factor(A11)                     (recursion)
 //     G12 = -G11 (P G22) = -G11 A12
 // All products run on the fp32 MFMA GEMM; blocks of at most 128 are factored and
-// inverted by one workgroup in registers.  Everything happens in the upper triangle of G;
+// inverted by one workgroup in LDS.  Everything happens in the upper triangle of G;
 // the strictly lower triangle is zeroed at the end.
 
 #include <climits>
@@ -90,144 +90,255 @@ dim3 rows_grid(int64_t rows, int64_t cols) {
   return dim3((unsigned)(gx < 1 ? 1 : gx > 64 ? 64 : gx), (unsigned)(rows > 32768 ? 32768 : rows));
 }
 
-// Factor the n x n diagonal block at (off, off) as U U^T (U upper) and overwrite its
-// upper triangle with G = U^-1.  One workgroup of 16 x 16 threads; thread (tx, ty) keeps
-// the 8 x 8 tile at rows 8ty.., cols 8tx.. of the symmetric block in registers.  Each
-// column step publishes one column (and, for the inverse, one row) through
-// double-buffered LDS, so a step costs one barrier plus at most 64 register FMAs.
-template <int KK>
-__device__ __forceinline__ void chol_step(float (&S)[8][8], int k, int tx, int ty, int i0, int j0,
-                                          float (*colbuf)[NB], float* diag, int* bad) {
-  const int b = k & 1;
-  if (tx == (k >> 3)) {
+// Factor the n x n diagonal block at (off, off) (n <= 128) as U U^T (U upper) and
+// overwrite its upper triangle with G = U^-1.  One workgroup of 4 waves; the block, padded
+// with the identity to 128, lives in LDS as its ten upper 32 x 32 sub-blocks.
+//
+// Sub-block p = 3, 2, 1, 0 (from the bottom right):
+//   diag   one wave factors the 32 x 32 Schur block S_pp and writes G_pp = U_pp^-1;
+//   row    G_pr = -G_pp T_pr for r > p, where T_pr = sum_{p<t<=r} U_pt G_tr;
+//   panel  U_qp = S_qp G_pp^T for q < p;
+//   update T_qp = U_qp G_pp, T_qr += U_qp G_pr (r > p), S_qt -= U_qp U_tp^T (q <= t < p).
+// Every product is one 32 x 32 x 32 v_mfma_f32_32x32x2_f32 sequence of one wave; the
+// products of a phase are spread over the four waves and phases are separated by
+// barriers.  Slot (q, r) holds S_qr, then T_qr, then G_qr; the panel U_qp has slots of
+// its own because the update phase reads it while overwriting slot (q, p).
+constexpr int LB = 32;              // sub-block
+constexpr int LS = LB + 1;          // LDS row stride: rows and columns both conflict-free
+constexpr int NLB = NB / LB;        // sub-blocks per side
+constexpr int NSLOT = NLB * (NLB + 1) / 2;
+constexpr int SLOT = LB * LS;
+
+__device__ __forceinline__ int slot_of(int q, int r) { return q * NLB - q * (q - 1) / 2 + (r - q); }
+
+// C = op(X) op(Y), C += op(X) op(Y) (ACC) or the same with the product negated (NEG),
+// for 32 x 32 blocks in LDS, one wave.
+//   op(X)[m][k] = TX ? X[k][m] : X[m][k],  op(Y)[k][n] = TY ? Y[n][k] : Y[k][n].
+// All operands are read into registers before the first MFMA (one LDS wait per product),
+// so C may alias X or Y.
+template <bool TX, bool TY, bool ACC, bool NEG>
+__device__ __forceinline__ void block_prod(float* C, const float* X, const float* Y, int lane) {
+  const int l32 = lane & 31, hi = lane >> 5;
+  float a[LB / 2], b[LB / 2], c[16];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) colbuf[b][i0 + r] = S[r][KK];
+  for (int kk = 0; kk < LB / 2; ++kk) {
+    const int k = 2 * kk + hi;
+    a[kk] = TX ? X[k * LS + l32] : X[l32 * LS + k];
+    b[kk] = TY ? Y[l32 * LS + k] : Y[k * LS + l32];
   }
-  __syncthreads();
-  const float piv = colbuf[b][k];
-  if (threadIdx.x == 0) {
-    diag[k] = piv;
-    if (!(piv > 0.0f) || !(piv < 3.0e38f)) *bad = k;
-  }
-  if (i0 < k && j0 < k) {
-    const float rp = 1.0f / piv;
-    // unconditional 16-byte loads (always in bounds), then masks: no branch per element
-    const floatx4* cv = reinterpret_cast<const floatx4*>(colbuf[b]);
-    const floatx4 i_lo = cv[i0 / 4], i_hi = cv[i0 / 4 + 1], j_lo = cv[j0 / 4], j_hi = cv[j0 / 4 + 1];
-    float ci[8], cj[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      ci[r] = (i0 + r < k) ? i_lo[r] : 0.0f;
-      ci[r + 4] = (i0 + r + 4 < k) ? i_hi[r] : 0.0f;
-      cj[r] = (j0 + r < k) ? j_lo[r] * rp : 0.0f;
-      cj[r + 4] = (j0 + r + 4 < k) ? j_hi[r] * rp : 0.0f;
-    }
+  for (int r = 0; r < 16; ++r) c[r] = ACC ? C[(8 * (r >> 2) + 4 * hi + (r & 3)) * LS + l32] : 0.0f;
+  __builtin_amdgcn_sched_barrier(0);   // keep every read ahead of the MFMA chain
+  floatx16 acc;
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
+  for (int r = 0; r < 16; ++r) acc[r] = NEG ? -c[r] : c[r];   // -(-C + XY) = C - XY
 #pragma unroll
-      for (int q = 0; q < 8; ++q) S[r][q] = fmaf(-ci[r], cj[q], S[r][q]);
-  }
+  for (int kk = 0; kk < LB / 2; ++kk)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[kk], b[kk], acc, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    C[(8 * (r >> 2) + 4 * hi + (r & 3)) * LS + l32] = NEG ? -acc[r] : acc[r];
 }
 
-template <int KK>
-__device__ __forceinline__ void inv_step(const float (&U)[8][8], float (&R)[8][8], int k, int tx,
-                                         int ty, int i0, int j0, float (*ucol)[NB],
-                                         float (*rrow)[NB], const float* diag) {
-  const int b = k & 1;
-  if (tx == (k >> 3)) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) ucol[b][i0 + r] = U[r][KK];
-  }
-  if (ty == (k >> 3)) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) rrow[b][j0 + q] = R[KK][q];
-  }
-  __syncthreads();
-  if (i0 < k) {
-    const float ru = 1.0f / diag[k];
-    const floatx4* uv = reinterpret_cast<const floatx4*>(ucol[b]);
-    const floatx4* rv = reinterpret_cast<const floatx4*>(rrow[b]);
-    const floatx4 u_lo = uv[i0 / 4], u_hi = uv[i0 / 4 + 1], g_lo = rv[j0 / 4], g_hi = rv[j0 / 4 + 1];
-    float uc[8], gk[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      uc[r] = (i0 + r < k) ? u_lo[r] : 0.0f;
-      uc[r + 4] = (i0 + r + 4 < k) ? u_hi[r] : 0.0f;
-      gk[r] = g_lo[r] * ru;
-      gk[r + 4] = g_hi[r] * ru;
-    }
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-      for (int q = 0; q < 8; ++q) R[r][q] = fmaf(-uc[r], gk[q], R[r][q]);
-  }
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
 
-__global__ void __launch_bounds__(256)
+// One wave: S (symmetric 32 x 32 at sp, only its upper triangle is read) = U U^T, U upper;
+// sp <- G = U^-1 (full block, zeros below the diagonal).  Reverse Gaussian elimination:
+// pivot k removes column k from rows i < k of S (rank-1 Schur update) and the same row
+// operation is applied to R (starting from I), so that R = L^-1 for S = L D L^T with L
+// unit upper; then G = D^-1/2 R.  Pivots are taken in pairs (k, k - 1): with
+// beta = S[k][k-1] / S[k][k], column k - 1 after the first update is c2 - beta c1 and its
+// pivot S[k-1][k-1] - beta S[k][k-1], so both updates are applied from one exchange.
+// Lane (j, h) holds column j and rows 2q + h (q = 0..15) of S and R.  Pair (2t+1, 2t) is
+// register t of half 1 and half 0, and the rows still active are registers q < t in both
+// halves.  Rows 2t+1 and 2t go through LDS in the order pos(i) = 16 (i & 1) + (i >> 1), so
+// that a lane reads its rows as consecutive words.
+// Returns the smallest k < k_valid whose pivot was not positive and finite, else -1.
+__device__ int diag_factor(float* sp, float* bc, int lane, int k_valid) {
+  const int j = lane & 31, h = lane >> 5;
+  const int pj = 16 * (j & 1) + (j >> 1);
+  float s[16], r[16], piv[16];   // piv[q]: 1 / sqrt(pivot) of this lane's row 2q + h
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int i = 2 * q + h;
+    s[q] = i <= j ? sp[i * LS + j] : sp[j * LS + i];
+    r[q] = (i == j) ? 1.0f : 0.0f;
+  }
+  int bad = -1;
+#pragma unroll
+  for (int t = LB / 2 - 1; t >= 0; --t) {
+    const int k = 2 * t + 1;
+    const float p1 = readlane_f(s[t], k + 32);      // S[k][k]
+    const float bk = readlane_f(s[t], k - 1 + 32);  // S[k][k-1]
+    const float p2 = readlane_f(s[t], k - 1);       // S[k-1][k-1]
+    const float rp1 = __builtin_amdgcn_rcpf(p1);
+    const float beta = bk * rp1;
+    const float p2s = fmaf(-beta, bk, p2);
+    const float rp2 = __builtin_amdgcn_rcpf(p2s);
+    if (k < k_valid && !(p1 > 0.0f && p1 < 3.0e38f)) bad = k;
+    if (k - 1 < k_valid && !(p2s > 0.0f && p2s < 3.0e38f)) bad = k - 1;
+    piv[t] = __builtin_amdgcn_rsqf(h ? p1 : p2s);   // D^-1/2 of this lane's row 2t + h
+    // half 1 publishes row k, half 0 row k - 1 (S masked to columns < k - 1)
+    bc[32 * h + pj] = (j < k - 1) ? s[t] : 0.0f;
+    bc[64 + 32 * h + pj] = r[t];
+    const float rk = bc[96 + pj];
+    const float rk1 = fmaf(-beta, rk, bc[64 + pj]);  // row k-1 of R after pivot k
+    r[t] = h ? r[t] : rk1;
+    if (t == 0) break;
+    float c1[16], c2[16];
+    const floatx4* v1 = reinterpret_cast<const floatx4*>(bc + 32 + 16 * h);
+    const floatx4* v2 = reinterpret_cast<const floatx4*>(bc + 16 * h);
+#pragma unroll
+    for (int v = 0; v < (t + 3) / 4; ++v) {
+      const floatx4 x1 = v1[v], x2 = v2[v];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { c1[4 * v + e] = x1[e]; c2[4 * v + e] = x2[e]; }
+    }
+    const float cj1 = bc[32 + pj];
+    const float cj2 = fmaf(-beta, cj1, bc[pj]);
+    const float a1 = cj1 * rp1, a2 = cj2 * rp2, g1 = rk * rp1, g2 = rk1 * rp2;
+#pragma unroll
+    for (int q = 0; q < t; ++q) {
+      const float c2s = fmaf(-beta, c1[q], c2[q]);
+      s[q] = fmaf(-c1[q], a1, s[q]);
+      s[q] = fmaf(-c2s, a2, s[q]);
+      r[q] = fmaf(-c1[q], g1, r[q]);
+      r[q] = fmaf(-c2s, g2, r[q]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) sp[(2 * q + h) * LS + j] = r[q] * piv[q];
+  return bad;
+}
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 leaf_factor_invert(float* __restrict__ A, int64_t ld, int64_t off, int n, int* flag) {
-  __shared__ __attribute__((aligned(16))) float colbuf[2][NB];
-  __shared__ __attribute__((aligned(16))) float rowbuf[2][NB];
-  __shared__ float diag[NB];
-  __shared__ int bad;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  const int i0 = 8 * ty, j0 = 8 * tx;
+  __shared__ float slot[NSLOT * SLOT];
+  __shared__ float ubuf[(NLB - 1) * SLOT];
+  __shared__ __attribute__((aligned(16))) float bc[128];
+  __shared__ int bad_at;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   float* blk = A + off * ld + off;
-  if (threadIdx.x == 0) bad = -1;
 
-  float S[8][8];
+  // Load the upper triangle into the slots: thread units of 4 consecutive columns of one
+  // row, every load issued before the first use (addresses clamped into the block, then
+  // selected); the padding beyond n is the identity.  Diagonal slots receive their upper
+  // triangle only (diag_factor reads no other part).
+  const bool vec = ((reinterpret_cast<uintptr_t>(blk) | (uintptr_t)(ld * 4)) & 15) == 0 &&
+                   (n & 3) == 0;
+  {
+    constexpr int UN = NB * NB / 4 / 256;
+    floatx4 v[UN];
+    if (vec) {
 #pragma unroll
-  for (int r = 0; r < 8; ++r)
+      for (int e = 0; e < UN; ++e) {
+        const int u = tid + 256 * e, i = u / (NB / 4), j0 = 4 * (u % (NB / 4));
+        const int ic = i < n ? i : n - 1, jc = j0 < n ? j0 : n - 4;
+        v[e] = *reinterpret_cast<const floatx4*>(blk + (ic * (int)ld + jc));
+      }
+    } else {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int i = i0 + r, j = j0 + q;
-      S[r][q] = (i < n && j < n) ? (j >= i ? blk[(int64_t)i * ld + j] : blk[(int64_t)j * ld + i])
-                                 : (i == j ? 1.0f : 0.0f);
+      for (int e = 0; e < UN; ++e) {
+        const int u = tid + 256 * e, i = u / (NB / 4), j0 = 4 * (u % (NB / 4));
+        const int ic = i < n ? i : n - 1;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int jc = j0 + c < n ? j0 + c : n - 1;
+          v[e][c] = blk[ic * (int)ld + jc];
+        }
+      }
     }
-
-  // A = U U^T from the bottom-right corner (outer-product form, columns unscaled).
-  for (int kb = NB / 8 - 1; kb >= 0; --kb) {
-#define GPTQ_CHOL(KK) \
-    if (8 * kb + KK < n) chol_step<KK>(S, 8 * kb + KK, tx, ty, i0, j0, colbuf, diag, &bad);
-    GPTQ_CHOL(7) GPTQ_CHOL(6) GPTQ_CHOL(5) GPTQ_CHOL(4)
-    GPTQ_CHOL(3) GPTQ_CHOL(2) GPTQ_CHOL(1) GPTQ_CHOL(0)
-#undef GPTQ_CHOL
-  }
-  __syncthreads();
-  if (threadIdx.x == 0 && bad >= 0) atomicMin(flag, (int)(off + bad) + 1);
-  for (int k = threadIdx.x; k < n; k += 256) diag[k] = sqrtf(diag[k]);
-  __syncthreads();
-  // scale to U: U[i][j] = S[i][j] / sqrt(p_j) above the diagonal, sqrt(p_j) on it
 #pragma unroll
-  for (int r = 0; r < 8; ++r)
+    for (int e = 0; e < UN; ++e) {
+      const int u = tid + 256 * e, i = u / (NB / 4), j0 = 4 * (u % (NB / 4));
+      if (j0 / LB < i / LB) continue;   // below the diagonal sub-blocks
+      float* d = slot + slot_of(i / LB, j0 / LB) * SLOT + (i % LB) * LS + j0 % LB;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int i = i0 + r, j = j0 + q;
-      const float dj = j < n ? diag[j] : 1.0f;
-      S[r][q] = i < j ? S[r][q] / dj : (i == j ? dj : 0.0f);
+      for (int c = 0; c < 4; ++c) {
+        const int jj = j0 + c;
+        d[c] = (i < n && jj < n) ? v[e][c] : (i == jj ? 1.0f : 0.0f);
+      }
     }
-
-  // U G = I from the bottom row up; R holds the rows of G not yet divided by U[i][i].
-  float R[8][8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r)
-#pragma unroll
-    for (int q = 0; q < 8; ++q) R[r][q] = (i0 + r == j0 + q) ? 1.0f : 0.0f;
-  for (int kb = NB / 8 - 1; kb >= 0; --kb) {
-#define GPTQ_INV(KK) \
-    if (8 * kb + KK < n) inv_step<KK>(S, R, 8 * kb + KK, tx, ty, i0, j0, colbuf, rowbuf, diag);
-    GPTQ_INV(7) GPTQ_INV(6) GPTQ_INV(5) GPTQ_INV(4)
-    GPTQ_INV(3) GPTQ_INV(2) GPTQ_INV(1) GPTQ_INV(0)
-#undef GPTQ_INV
   }
+  if (tid == 0) bad_at = INT_MAX;
+  __syncthreads();
+
+  // Iteration p: wave 0 applies the last Schur update of S_pp (from the panel of p + 1) and
+  // factors it while waves 1-3 run the other update products of p + 1; then all waves form
+  // row p of G and the panel of p.
+  for (int p = NLB - 1; p >= 0; --p) {
+    const float* gpp = slot + slot_of(p, p) * SLOT;
+    if (wave == 0) {
+      float* spp = slot + slot_of(p, p) * SLOT;
+      if (p + 1 < NLB) {                                  // S_pp -= U_p U_p^T
+        const float* u = ubuf + p * SLOT;
+        block_prod<false, true, true, true>(spp, u, u, lane);
+      }
+      const int b = diag_factor(spp, bc, lane, n - LB * p);
+      if (b >= 0 && lane == 0) bad_at = min(bad_at, LB * p + b);
+    } else if (p + 1 < NLB) {
+      const int pp = p + 1;                               // update products of step p + 1
+      const float* gq = slot + slot_of(pp, pp) * SLOT;
+      int task = 0;
+      for (int q = 0; q < pp; ++q) {
+        const float* u = ubuf + q * SLOT;
+        if (task++ % 3 == wave - 1)                      // T_q,pp = U_q G_pp,pp
+          block_prod<false, false, false, false>(slot + slot_of(q, pp) * SLOT, u, gq, lane);
+        for (int r = pp + 1; r < NLB; ++r)               // T_qr += U_q G_pp,r
+          if (task++ % 3 == wave - 1)
+            block_prod<false, false, true, false>(slot + slot_of(q, r) * SLOT, u,
+                                                  slot + slot_of(pp, r) * SLOT, lane);
+        for (int t = q; t < pp; ++t)                     // S_qt -= U_q U_t^T (but S_pp)
+          if (!(q == p && t == p) && task++ % 3 == wave - 1)
+            block_prod<false, true, true, true>(slot + slot_of(q, t) * SLOT, u, ubuf + t * SLOT,
+                                                lane);
+      }
+    }
+    __syncthreads();
+    int task = 0;
+    for (int r = p + 1; r < NLB; ++r, ++task)            // G_pr = -G_pp T_pr
+      if (task % 4 == wave) {
+        float* c = slot + slot_of(p, r) * SLOT;
+        block_prod<false, false, false, true>(c, gpp, c, lane);
+      }
+    for (int q = 0; q < p; ++q, ++task)                  // U_qp = S_qp G_pp^T
+      if (task % 4 == wave)
+        block_prod<false, true, false, false>(ubuf + q * SLOT, slot + slot_of(q, p) * SLOT, gpp,
+                                              lane);
+    __syncthreads();
+  }
+
+  if (tid == 0 && bad_at != INT_MAX) atomicMin(flag, (int)(off + bad_at) + 1);
+  // Store whole rows of the block: the upper sub-blocks from the slots (diagonal ones hold
+  // zeros below the diagonal), zeros for the sub-blocks below them.  Entries below the
+  // diagonal of the matrix are don't-care until the final clearing pass.
+  {
+    constexpr int UN = NB * NB / 4 / 256;
+    floatx4 g[UN];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int i = i0 + r;
-    if (i >= n) continue;
-    const float ru = 1.0f / diag[i];
+    for (int e = 0; e < UN; ++e) {
+      const int u = tid + 256 * e, i = u / (NB / 4), j0 = 4 * (u % (NB / 4));
+      const int bi = i / LB, bj = j0 / LB < bi ? bi : j0 / LB;
+      const float* src = slot + slot_of(bi, bj) * SLOT + (i % LB) * LS + j0 % LB;
+      const bool up = j0 / LB >= bi;
+      g[e] = floatx4{up ? src[0] : 0.0f, up ? src[1] : 0.0f, up ? src[2] : 0.0f,
+                     up ? src[3] : 0.0f};
+    }
+    const int ld32 = (int)ld;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int j = j0 + q;
-      if (j >= i && j < n) blk[(int64_t)i * ld + j] = R[r][q] * ru;
+    for (int e = 0; e < UN; ++e) {
+      const int u = tid + 256 * e, i = u / (NB / 4), j0 = 4 * (u % (NB / 4));
+      float* dst = blk + (i * ld32 + j0);
+      if (vec) {
+        if (i < n && j0 < n) *reinterpret_cast<floatx4*>(dst) = g[e];
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (i < n && j0 + c < n) dst[c] = g[e][c];
+      }
     }
   }
 }
