@@ -155,11 +155,13 @@ int gptq_dequant_check(const uint32_t* qweight, const float* scales, const uint8
 
 /* ---------------------------------------------------------------- instrumentation
  * Optional per-kernel timing with HIP events recorded on the caller's stream around
- * every launch of the named kernel family ("hessian_mfma", "hessian_reduce", "prep",
- * "quant_block", "lazy_gemm", ...).  Enabling costs two event records per launch.
+ * every launch of the named kernel family ("hessian_mfma", "hessian_reduce", "prep_leaf",
+ * "prep_gemm", "quant_block", "lazy_gemm", ...).  Enabling costs two event records per
+ * timed launch; gptq_profile_only(name) restricts timing to one family (NULL: all).
  * gptq_profile_read returns the number of timed launches and their summed duration in
- * milliseconds (waits for the recorded events).  Not thread-safe; for measurement. */
+ * milliseconds (waits for the recorded events).  For measurement, not for production. */
 int gptq_profile_enable(int on);
+int gptq_profile_only(const char* kernel);
 int gptq_profile_reset(void);
 int gptq_profile_read(const char* kernel, int64_t* launches, double* total_ms);
 

@@ -47,8 +47,20 @@ struct ProfTotal {
 };
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+std::string g_prof_only;                // empty: every kernel family
 std::vector<PendingEvent> g_pending;
+std::vector<hipEvent_t> g_free_events;  // recycled, so a timed launch costs two records only
 std::map<std::string, ProfTotal> g_totals;
+
+hipEvent_t take_event() {   // caller holds g_prof_mu
+  if (!g_free_events.empty()) {
+    hipEvent_t e = g_free_events.back();
+    g_free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  return hipEventCreate(&e) == hipSuccess ? e : nullptr;
+}
 
 void drain_pending() {
   for (auto& p : g_pending) {
@@ -58,8 +70,8 @@ void drain_pending() {
       t.launches += 1;
       t.ms += ms;
     }
-    (void)hipEventDestroy(p.e0);
-    (void)hipEventDestroy(p.e1);
+    g_free_events.push_back(p.e0);
+    g_free_events.push_back(p.e1);
   }
   g_pending.clear();
 }
@@ -97,10 +109,12 @@ namespace gptq {
 
 ProfScope::ProfScope(const char* n, hipStream_t s) : name(n), stream(s), ev0(nullptr) {
   if (!g_prof_on) return;
-  hipEvent_t e;
-  if (hipEventCreate(&e) != hipSuccess) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_only.empty() && g_prof_only != n) return;
+  hipEvent_t e = take_event();
+  if (!e) return;
   if (hipEventRecord(e, s) != hipSuccess) {
-    (void)hipEventDestroy(e);
+    g_free_events.push_back(e);
     return;
   }
   ev0 = e;
@@ -108,12 +122,13 @@ ProfScope::ProfScope(const char* n, hipStream_t s) : name(n), stream(s), ev0(nul
 
 ProfScope::~ProfScope() {
   if (!ev0) return;
-  hipEvent_t e1;
-  if (hipEventCreate(&e1) != hipSuccess || hipEventRecord(e1, stream) != hipSuccess) {
-    (void)hipEventDestroy(static_cast<hipEvent_t>(ev0));
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  hipEvent_t e1 = take_event();
+  if (!e1 || hipEventRecord(e1, stream) != hipSuccess) {
+    g_free_events.push_back(static_cast<hipEvent_t>(ev0));
+    if (e1) g_free_events.push_back(e1);
     return;
   }
-  std::lock_guard<std::mutex> lk(g_prof_mu);
   g_pending.push_back({name, static_cast<hipEvent_t>(ev0), e1});
 }
 
@@ -259,6 +274,12 @@ int gptq_dequant_check(const uint32_t* qweight, const float* scales, const uint8
 int gptq_profile_enable(int on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = on != 0;
+  return GPTQ_OK;
+}
+
+int gptq_profile_only(const char* kernel) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_only = kernel ? kernel : "";
   return GPTQ_OK;
 }
 

@@ -52,6 +52,7 @@ _SIGS = {
     "gptq_dequant_check": ([_vp, _vp, _vp, _vp, _int, _vp, _i64, _i64, ctypes.POINTER(Spec), _vp,
                             _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "gptq_profile_enable": ([_int], _int),
+    "gptq_profile_only": ([ctypes.c_char_p], _int),
     "gptq_profile_reset": ([], _int),
     "gptq_profile_read": ([ctypes.c_char_p, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double)], _int),
 }
@@ -200,6 +201,11 @@ def dequant_check(qweight, scales, zeros, W, H, spec: Spec, want_w_hat=False, ws
 
 def profile_enable(on=True):
     _check(lib().gptq_profile_enable(int(bool(on))))
+
+
+def profile_only(kernel=None):
+    """Time only the named kernel family (None: all families)."""
+    _check(lib().gptq_profile_only(kernel.encode() if kernel else None))
 
 
 def profile_reset():
