@@ -237,6 +237,237 @@ __global__ void __launch_bounds__(256, 2) gemm_f32_mfma(Dev g) {
       }
 }
 
+// ---------------------------------------------------------------------------------
+// Direct-to-LDS variant (op(A) = A row-major M x K; B row-major K x N, or N x K with TB).
+// Operand tiles of 16 k per stage are copied from global memory straight into LDS by
+// buffer loads (`buffer_load_dwordx4 ... lds`, 1 KB per wave instruction), four stages in
+// the ring and three in flight, one barrier per stage.  A k-contiguous tile (A, or B with
+// TB) keeps 64-byte rows of 4 16-byte chunks whose slot is XOR-swizzled by (row / 4) % 4,
+// so a ds_read_b128 of one chunk per lane is conflict-free; an n-contiguous tile (B) keeps
+// its k rows with 64 or 128 bytes of padding per 1 KB copy, so that the two lane halves
+// (k and k + 4) read disjoint banks.  MFMA k index: lane half h, step 4u + e of a stage
+// uses k = 4 (2u + h) + e, which lets the k-contiguous operand deliver four steps per
+// 16-byte read.  Global addresses are clamped into the operands and the stages that touch
+// an edge or a triangular mask zero the affected values after the LDS read.
+typedef uint32_t rsrc_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return rsrc_t{lo, hi & 0xffffu, 0xffffffffu, 0x00020000u};
+}
+
+// One wave-wide 1 KB copy: lane l's 16 bytes at byte offset voff land at lds_base + 16 l.
+// Inline asm keeps the compiler from treating later LDS reads as dependent on the copy
+// (it would wait for the whole ring); explicit vmcnt waits before each stage barrier
+// order the copies.  No register output.
+__device__ __forceinline__ void dma16(rsrc_t rsrc, uint32_t lds_base, int voff) {
+  __asm__ volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                   :
+                   : "v"(voff), "s"(rsrc), "s"(lds_base)
+                   : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt((15 & 15) | (3 << 14) | (7 << 4) | (0 << 8));
+  __builtin_amdgcn_s_barrier();
+}
+
+constexpr int DBK = 16;   // k per stage
+constexpr int DNS = 4;    // stages in the ring
+
+// n-contiguous tile of width W floats: rows per 1 KB copy, padding per copy, bytes
+__host__ __device__ constexpr int nc_rows(int W) { return 256 / W; }
+__host__ __device__ constexpr int nc_pad(int W) { return W == 128 ? 64 : 128; }
+__host__ __device__ constexpr int nc_bytes(int W) { return (DBK / nc_rows(W)) * (1024 + nc_pad(W)); }
+
+template <int BM, int BN, bool TB>
+struct DCfg {
+  static constexpr int A_BYTES = BM * 64;                        // k-contiguous
+  static constexpr int B_BYTES = TB ? BN * 64 : nc_bytes(BN);
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_COPIES = BM / 16, B_COPIES = BN / 16;   // 1 KB copies per stage
+  static constexpr int CPW = (A_COPIES + B_COPIES) / 4;          // per wave
+  static constexpr int TM = BM / 64, TN = BN / 64;
+  static_assert((A_COPIES + B_COPIES) % 4 == 0, "copies must split over 4 waves");
+};
+
+// k-contiguous tile of `rows` rows starting at element `base` (row stride ld): copy q.
+// Rows >= row_lim and k >= k_lim are clamped (their values are masked later).
+__device__ __forceinline__ void copy_kc(rsrc_t rsrc, uint32_t lds, int q, int lane, int ld,
+                                        int row_lim, int k_lim) {
+  const int row = 16 * q + (lane >> 2);
+  const int c = (lane & 3) ^ ((row >> 2) & 3);
+  const int r = row < row_lim ? row : row_lim - 1;
+  const int k = 4 * c < k_lim ? 4 * c : k_lim - 4;
+  dma16(rsrc, lds + q * 1024, (r * ld + k) * 4);
+}
+// n-contiguous tile (DBK rows of W floats): copy q.
+template <int W>
+__device__ __forceinline__ void copy_nc(rsrc_t rsrc, uint32_t lds, int q, int lane, int ld,
+                                        int k_lim, int n_lim) {
+  constexpr int CH = W / 4;
+  const int kr = q * nc_rows(W) + lane / CH;
+  const int ch = lane % CH;
+  const int k = kr < k_lim ? kr : k_lim - 1;
+  const int n = 4 * ch < n_lim ? 4 * ch : n_lim - 4;
+  dma16(rsrc, lds + q * (1024 + nc_pad(W)), (k * ld + n) * 4);
+}
+
+template <int BM, int BN, bool TB>
+__global__ void __launch_bounds__(256, 2) gemm_f32_dma(Dev g) {
+  using C = DCfg<BM, BN, TB>;
+  __shared__ __attribute__((aligned(1024))) char ring[DNS * C::STAGE];
+
+  const int64_t tiles_n = (g.N + BN - 1) / BN;
+  const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * BM;
+  const int64_t n0 = (int64_t)(blockIdx.x % tiles_n) * BN;
+  if (g.triC == 1 && m0 >= n0 + BN) return;  // tile entirely below the diagonal
+
+  int64_t k_lo = 0, k_hi = g.K;
+  if (g.triA == 1) k_lo = m0;
+  if (g.triA == 2) k_hi = k_hi < m0 + BM ? k_hi : m0 + BM;
+  if (g.triB == 1) k_hi = k_hi < n0 + BN ? k_hi : n0 + BN;
+  if (g.triB == 2) k_lo = k_lo > n0 ? k_lo : n0;
+  k_lo = k_lo / DBK * DBK;
+  const int nsteps = k_hi > k_lo ? (int)((k_hi - k_lo + DBK - 1) / DBK) : 0;
+
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m_left = (int)(g.M - m0 < BM ? g.M - m0 : BM);
+  const int n_left = (int)(g.N - n0 < BN ? g.N - n0 : BN);
+  const bool edge_mn = m_left < BM || n_left < BN;
+  const uint32_t ring0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)ring);
+  const int lda = (int)g.lda, ldb = (int)g.ldb;
+
+  auto issue = [&](int st) {
+    const int64_t k0 = k_lo + (int64_t)st * DBK;
+    const int k_lim = (int)(g.K - k0 < DBK ? g.K - k0 : DBK);
+    const uint32_t sa = ring0 + (st % DNS) * C::STAGE, sb = sa + C::A_BYTES;
+    const rsrc_t ra = make_rsrc(g.A + m0 * g.lda + k0);
+    const rsrc_t rb = make_rsrc(TB ? g.B + n0 * g.ldb + k0 : g.B + k0 * g.ldb + n0);
+#pragma unroll
+    for (int i = 0; i < C::CPW; ++i) {
+      const int q = wave * C::CPW + i;             // copy index over A then B
+      if (q < C::A_COPIES) {
+        copy_kc(ra, sa, q, lane, lda, m_left, k_lim);
+      } else if (TB) {
+        copy_kc(rb, sb, q - C::A_COPIES, lane, ldb, n_left, k_lim);
+      } else {
+        copy_nc<BN>(rb, sb, q - C::A_COPIES, lane, ldb, k_lim, n_left);
+      }
+    }
+  };
+  // does stage st need masking (an edge, the end of K, or a triangle's diagonal)?
+  auto masked = [&](int st) {
+    const int64_t k0 = k_lo + (int64_t)st * DBK;
+    if (edge_mn || k0 + DBK > g.K || k0 < k_lo) return true;
+    if (g.triA == 1 && k0 < m0 + BM) return true;
+    if (g.triA == 2 && k0 + DBK > m0) return true;
+    if (g.triB == 1 && k0 + DBK > n0) return true;
+    if (g.triB == 2 && k0 < n0 + BN) return true;
+    return false;
+  };
+
+  floatx16 acc[C::TM][C::TN];
+#pragma unroll
+  for (int x = 0; x < C::TM; ++x)
+#pragma unroll
+    for (int y = 0; y < C::TN; ++y)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.0f;
+
+  if (nsteps > 0) issue(0);
+  if (nsteps > 1) issue(1);
+  if (nsteps > 2) issue(2);
+  for (int s = 0; s < nsteps; ++s) {
+    const int later = nsteps - 1 - s < 2 ? nsteps - 1 - s : 2;
+    if (later == 2) wait_vmcnt<2 * C::CPW>();
+    else if (later == 1) wait_vmcnt<C::CPW>();
+    else wait_vmcnt<0>();
+    stage_barrier();
+    if (s + 3 < nsteps) issue(s + 3);   // into the buffer read in iteration s - 1
+    const char* sa = ring + (s % DNS) * C::STAGE;
+    const char* sb = sa + C::A_BYTES;
+    const int64_t k0 = k_lo + (int64_t)s * DBK;
+    const bool msk = masked(s);
+#pragma unroll
+    for (int u = 0; u < DBK / 8; ++u) {
+      const int c = 2 * u + h;                     // chunk: k = 4c .. 4c + 3
+      floatx4 a[C::TM];
+#pragma unroll
+      for (int x = 0; x < C::TM; ++x) {
+        const int row = wm * (BM / 2) + 32 * x + l32;
+        a[x] = *reinterpret_cast<const floatx4*>(sa + row * 64 + 16 * (c ^ ((row >> 2) & 3)));
+        if (msk) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t mg = m0 + row, kg = k0 + 4 * c + e;
+            if (!a_ok(g, mg, kg) || kg < k_lo) a[x][e] = 0.0f;
+          }
+        }
+        a[x] = a[x] * g.alpha;
+      }
+      floatx4 b[C::TN];
+#pragma unroll
+      for (int y = 0; y < C::TN; ++y) {
+        const int col = wn * (BN / 2) + 32 * y + l32;
+        if (TB) {
+          b[y] = *reinterpret_cast<const floatx4*>(sb + col * 64 + 16 * (c ^ ((col >> 2) & 3)));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int kr = 4 * c + e;
+            b[y][e] = *reinterpret_cast<const float*>(
+                sb + (kr / nc_rows(BN)) * (1024 + nc_pad(BN)) + (kr % nc_rows(BN)) * BN * 4 + col * 4);
+          }
+        }
+        if (msk) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t kg = k0 + 4 * c + e, ng = n0 + col;
+            if (!b_ok(g, kg, ng) || kg < k_lo) b[y][e] = 0.0f;
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int x = 0; x < C::TM; ++x)
+#pragma unroll
+          for (int y = 0; y < C::TN; ++y)
+            acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[x][e], b[y][e], acc[x][y], 0, 0, 0);
+    }
+  }
+
+  // epilogue: C = alpha op(A) op(B) (+ C when beta = 1); alpha was applied to op(A)
+  float* ct = g.C + m0 * g.ldc + n0;
+  const int ldc = (int)g.ldc;
+  const int diag_off = (int)(n0 - m0);   // m <= n  <=>  mr <= nc + diag_off
+  const bool acc_c = g.beta != 0.0f;
+#pragma unroll
+  for (int x = 0; x < C::TM; ++x)
+#pragma unroll
+    for (int y = 0; y < C::TN; ++y)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int mr = wm * (BM / 2) + 32 * x + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int nc = wn * (BN / 2) + 32 * y + l32;
+        if (mr < m_left && nc < n_left && (g.triC == 0 || mr <= nc + diag_off)) {
+          float v = acc[x][y][r];
+          if (acc_c) v += ct[mr * ldc + nc];
+          ct[mr * ldc + nc] = v;
+        }
+      }
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 template <int BM, int BN>
@@ -246,6 +477,14 @@ hipError_t launch(const Dev& g, bool ta, bool tb, hipStream_t s) {
   else if (!ta && tb) hipLaunchKernelGGL((gemm_f32_mfma<BM, BN, false, true>), dim3(grid), dim3(256), 0, s, g);
   else if (ta && !tb) hipLaunchKernelGGL((gemm_f32_mfma<BM, BN, true, false>), dim3(grid), dim3(256), 0, s, g);
   else hipLaunchKernelGGL((gemm_f32_mfma<BM, BN, true, true>), dim3(grid), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+template <int BM, int BN>
+hipError_t launch_dma(const Dev& g, bool tb, hipStream_t s) {
+  const int64_t grid = ceil_div(g.M, BM) * ceil_div(g.N, BN);
+  if (tb) hipLaunchKernelGGL((gemm_f32_dma<BM, BN, true>), dim3(grid), dim3(256), 0, s, g);
+  else hipLaunchKernelGGL((gemm_f32_dma<BM, BN, false>), dim3(grid), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
@@ -266,6 +505,15 @@ hipError_t gemm_f32(const GemmArgs& a, hipStream_t stream, const char* prof_name
         vec};
   ProfScope ps(prof_name, stream);
   const int64_t big_tiles = ceil_div(a.M, 128) * ceil_div(a.N, 128);
+  // direct-to-LDS path: A row-major, 16-byte rows and chunks that do not straddle an edge
+  // (byte offsets inside a 128-row tile stay below 2^31 for leading dimensions < 2^21)
+  const bool dma = vec && !a.transA && a.K % 4 == 0 && a.K >= 4 && (a.transB || a.N % 4 == 0) &&
+                   a.M >= 64 && a.N >= 64 && a.lda < ((int64_t)1 << 21) &&
+                   a.ldb < ((int64_t)1 << 21);
+  if (dma) {
+    if (big_tiles >= 192) return launch_dma<128, 128>(g, a.transB, stream);
+    return launch_dma<64, 64>(g, a.transB, stream);
+  }
   if (big_tiles >= 192) return launch<128, 128>(g, a.transA, a.transB, stream);
   return launch<64, 64>(g, a.transA, a.transB, stream);
 }

@@ -241,7 +241,8 @@ quant_block(const float* __restrict__ Wc, const float* __restrict__ G, int64_t d
   __syncthreads();
 
   quant_steps<B>(r, gl, rinv, c, bits, sym, g, width, j0, scales, zeros, n_groups, row, row_ok,
-                 cbuf + rl * B, E + (row_ok ? row : 0) * B, std::make_integer_sequence<int, B>{});
+                 cbuf + rl * B, E + (row_ok ? row : 0) * d_col + j0,
+                 std::make_integer_sequence<int, B>{});
 
   if (row_ok && c == 0 && err_sq) err_sq[row] += (double)r.esq;
   // pack: each lane assembles whole 32-bit words from the row's code bytes in LDS
@@ -292,9 +293,49 @@ hipError_t launch_block(const QuantArgs& a, const float* Wc, float* E, int64_t j
 }  // namespace
 
 size_t quant_ws_bytes(int64_t d_row, int64_t d_col, int block) {
-  return align_up((size_t)d_row * d_col * sizeof(float), 256) +
-         align_up((size_t)d_row * block * sizeof(float), 256);
+  (void)block;
+  // working copy of W and the errors E of every column, both d_row x d_col float32
+  return 2 * align_up((size_t)d_row * d_col * sizeof(float), 256);
 }
+
+namespace {
+
+// Columns [c0, c0 + n) with every update from the columns left of c0 already applied.
+// The lazy batch update is applied recursively: after the left half of the range is
+// quantized, its errors update the right half in one product (K = left width), so each
+// weight is rewritten once per level (log2 of the block count) instead of once per block,
+// and the products are large.  The sum of the products equals the per-block updates
+// W[:, j+B:] -= E_j G[j:j+B, j+B:] of all blocks j.
+hipError_t solve(const QuantArgs& a, float* Wc, float* E, int64_t c0, int64_t n, int64_t g,
+                 int64_t n_groups, hipStream_t s) {
+  hipError_t e;
+  if (n <= a.block) {
+    if (g > a.block && c0 % g == 0) {
+      ProfScope ps("quant_group_params", s);
+      hipLaunchKernelGGL(group_params, dim3((unsigned)ceil_div(a.d_row, 4)), dim3(256), 0, s, Wc,
+                         a.d_row, a.d_col, c0, g, a.bits, a.sym, a.scales, a.zeros, n_groups);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    ProfScope ps("quant_block", s);
+    switch (a.block) {
+      case 32: return launch_block<32>(a, Wc, E, c0, (int)n, s);
+      case 64: return launch_block<64>(a, Wc, E, c0, (int)n, s);
+      case 128: return launch_block<128>(a, Wc, E, c0, (int)n, s);
+      case 256: return launch_block<256>(a, Wc, E, c0, (int)n, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  const int64_t h = ceil_div(n, a.block) / 2 * a.block;
+  if ((e = solve(a, Wc, E, c0, h, g, n_groups, s)) != hipSuccess) return e;
+  // W[:, c0+h : c0+n] -= E[:, c0 : c0+h] G[c0 : c0+h, c0+h : c0+n]
+  GemmArgs ga{a.d_row, n - h, h, E + c0, a.d_col, 0, 0,
+              a.G + c0 * a.d_col + c0 + h, a.d_col, 0, 0,
+              Wc + c0 + h, a.d_col, 0, -1.0f, 1.0f};
+  if ((e = gemm_f32(ga, s, "lazy_gemm")) != hipSuccess) return e;
+  return solve(a, Wc, E, c0 + h, n - h, g, n_groups, s);
+}
+
+}  // namespace
 
 hipError_t quant_launch(const QuantArgs& a, void* ws, hipStream_t s) {
   hipError_t e;
@@ -314,36 +355,7 @@ hipError_t quant_launch(const QuantArgs& a, void* ws, hipStream_t s) {
     }
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-
-  for (int64_t j0 = 0; j0 < a.d_col; j0 += a.block) {
-    const int width = (int)(a.d_col - j0 < a.block ? a.d_col - j0 : a.block);
-    if (g > a.block && j0 % g == 0) {
-      ProfScope ps("quant_group_params", s);
-      hipLaunchKernelGGL(group_params, dim3((unsigned)ceil_div(a.d_row, 4)), dim3(256), 0, s, Wc,
-                         a.d_row, a.d_col, j0, g, a.bits, a.sym, a.scales, a.zeros, n_groups);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    {
-      ProfScope ps("quant_block", s);
-      switch (a.block) {
-        case 32: e = launch_block<32>(a, Wc, E, j0, width, s); break;
-        case 64: e = launch_block<64>(a, Wc, E, j0, width, s); break;
-        case 128: e = launch_block<128>(a, Wc, E, j0, width, s); break;
-        case 256: e = launch_block<256>(a, Wc, E, j0, width, s); break;
-        default: e = hipErrorInvalidValue;
-      }
-      if (e != hipSuccess) return e;
-    }
-    const int64_t rest = a.d_col - j0 - width;
-    if (rest > 0) {
-      // W[:, j0+w:] -= E[:, :w] G[j0:j0+w, j0+w:]
-      GemmArgs ga{a.d_row, rest, width, E, a.block, 0, 0,
-                  a.G + j0 * a.d_col + j0 + width, a.d_col, 0, 0,
-                  Wc + j0 + width, a.d_col, 0, -1.0f, 1.0f};
-      if ((e = gemm_f32(ga, s, "lazy_gemm")) != hipSuccess) return e;
-    }
-  }
-  return hipSuccess;
+  return solve(a, Wc, E, 0, a.d_col, g, n_groups, s);
 }
 
 }  // namespace gptq
