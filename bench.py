@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=64)
     p.add_argument("--traffic", default=None,
                    help="JSON file with HBM bytes per launch of the dominant kernel (rocprofv3 pmc)")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="before the steps, run one elementwise copy (torch.neg) of this many MiB: "
+                        "the reference dispatch for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     return p.parse_args()
 
 
@@ -142,6 +145,14 @@ def main():
         G.prepare_hinv(H, G=Gm, damp_frac=wl.damp, ws=ws_p, check=check)
         G.quantize_layer(Wd, Gm, spec, qweight=qweight, scales=scales, zeros=zeros, err_sq=esq,
                          ws=ws_q)
+
+    if a.calib_copy_mib:
+        src = torch.ones(a.calib_copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)          # reads and writes calib_copy_mib MiB each
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(a.warmup):
         step(True)
