@@ -40,14 +40,44 @@ def parse():
     p.add_argument("--bits", type=int, default=None)
     p.add_argument("--block", type=int, default=None)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--cpu-tokens", type=int, default=8192)
-    p.add_argument("--cpu-rows", type=int, default=64)
-    p.add_argument("--traffic", default=None,
-                   help="JSON file with HBM bytes per launch of the dominant kernel (rocprofv3 pmc)")
+    p.add_argument("--cpu-tokens", type=int, default=16384)
+    p.add_argument("--cpu-rows", type=int, default=128)
+    p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                   help="JSON with the HBM bytes per launch of kernel families, from rocprofv3 "
+                        "FETCH_SIZE/WRITE_SIZE passes; used only while the kernel source is unchanged")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="before the steps, run one elementwise copy (torch.neg) of this many MiB: "
                         "the reference dispatch for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     return p.parse_args()
+
+
+KERNEL_SOURCE = {   # kernel family -> the source file its counters were taken from
+    "hessian_mfma": "hessian.hip", "hessian_reduce": "hessian.hip", "prep_leaf": "prep.hip",
+    "prep_gemm": "gemm.hip", "lazy_gemm": "gemm.hip", "quant_block": "quant.hip",
+}
+
+
+def source_sha256(name):
+    import hashlib
+    path = os.path.join(ROOT, "post_weight_quantization_24_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def kernel_traffic(path, family, **cfg):
+    """HBM bytes per launch of `family` measured with rocprofv3 counters (profiles/), or None
+    when there is no measurement for this workload or the kernel source has changed since."""
+    if not path or not os.path.exists(path) or family not in KERNEL_SOURCE:
+        return None
+    with open(path) as f:
+        table = json.load(f)
+    for e in table.get("entries", []):
+        if e.get("kernel") != family or any(e.get(k) != v for k, v in cfg.items()):
+            continue
+        if e.get("source_sha256") != source_sha256(KERNEL_SOURCE[family]):
+            return None
+        return e["hbm_bytes_per_launch"]
+    return None
 
 
 def cpu_baseline(W, X_sample, n_tok_full, spec, rows):
@@ -207,11 +237,8 @@ def main():
     else:
         work, unit, peak, bound = None, "TFLOP/s", PEAK["mfma_f32"], "mfma"
         achieved = 0.0
-    traffic = None
-    if a.traffic and os.path.exists(a.traffic):
-        with open(a.traffic) as f:
-            tr = json.load(f)
-        traffic = tr.get(dom)
+    traffic = kernel_traffic(a.traffic, dom, workload=wl.name, layer=layer.name, bits=bits,
+                             block=block)
     roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                 "frac": achieved / peak, "traffic": traffic, "kernel": dom}
 
