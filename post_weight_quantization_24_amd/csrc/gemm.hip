@@ -66,16 +66,26 @@ __device__ __forceinline__ bool b_ok(const Dev& g, int64_t k, int64_t n) {
   return true;
 }
 
+// LDS of one workgroup: two stages of op(A) and op(B), k-major.
+template <int BM, int BN>
+struct Smem {
+  static constexpr int BK = BM >= 128 ? 16 : 32;
+  float a[2][BK * (BM + 4)];
+  float b[2][BK * (BN + 4)];
+};
+
+// Output tile `tile` (row-major over the tile grid) of one problem.
 template <int BM, int BN, bool TA, bool TB>
-__global__ void __launch_bounds__(256, 2) gemm_f32_mfma(Dev g) {
+__device__ __forceinline__ void gemm_tile(const Dev& g, int64_t tile, Smem<BM, BN>& sm) {
   using C = Cfg<BM, BN, TA, TB>;
   constexpr int BK = C::BK;
-  __shared__ __attribute__((aligned(16))) float As[2][BK * C::LDA_S];
-  __shared__ __attribute__((aligned(16))) float Bs[2][BK * C::LDB_S];
+  static_assert(BK == Smem<BM, BN>::BK, "stage depth");
+  auto& As = sm.a;
+  auto& Bs = sm.b;
 
   const int64_t tiles_n = (g.N + BN - 1) / BN;
-  const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * BM;
-  const int64_t n0 = (int64_t)(blockIdx.x % tiles_n) * BN;
+  const int64_t m0 = (int64_t)(tile / tiles_n) * BM;
+  const int64_t n0 = (int64_t)(tile % tiles_n) * BN;
   if (g.triC == 1 && m0 >= n0 + BN) return;  // tile entirely below the diagonal
 
   int64_t k_lo = 0, k_hi = g.K;
@@ -235,6 +245,21 @@ __global__ void __launch_bounds__(256, 2) gemm_f32_mfma(Dev g) {
         if (mr < m_left && nc < n_left && (g.triC == 0 || mr <= nc + diag_off))
           ct[mr * ldc + nc] = out_scale * acc[x][y][r];
       }
+}
+
+template <int BM, int BN, bool TA, bool TB>
+__global__ void __launch_bounds__(256, 2) gemm_f32_mfma(Dev g) {
+  __shared__ __attribute__((aligned(16))) Smem<BM, BN> sm;
+  gemm_tile<BM, BN, TA, TB>(g, blockIdx.x, sm);
+}
+
+// Two independent problems in one launch (tiles of the first, then of the second); both
+// have op(A) = A and share the tile shape and the LDS.
+template <int BM, int BN, bool TB1, bool TB2>
+__global__ void __launch_bounds__(256, 2) gemm_f32_pair(Dev g1, int64_t tiles1, Dev g2) {
+  __shared__ __attribute__((aligned(16))) Smem<BM, BN> sm;
+  if ((int64_t)blockIdx.x < tiles1) gemm_tile<BM, BN, false, TB1>(g1, blockIdx.x, sm);
+  else gemm_tile<BM, BN, false, TB2>(g2, (int64_t)blockIdx.x - tiles1, sm);
 }
 
 // ---------------------------------------------------------------------------------
@@ -488,7 +513,43 @@ hipError_t launch_dma(const Dev& g, bool tb, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int BM, int BN>
+hipError_t launch_pair(const Dev& g1, bool tb1, const Dev& g2, bool tb2, hipStream_t s) {
+  const int64_t t1 = ceil_div(g1.M, BM) * ceil_div(g1.N, BN);
+  const int64_t grid = t1 + ceil_div(g2.M, BM) * ceil_div(g2.N, BN);
+  if (!tb1 && !tb2) hipLaunchKernelGGL((gemm_f32_pair<BM, BN, false, false>), dim3(grid), dim3(256), 0, s, g1, t1, g2);
+  else if (!tb1 && tb2) hipLaunchKernelGGL((gemm_f32_pair<BM, BN, false, true>), dim3(grid), dim3(256), 0, s, g1, t1, g2);
+  else if (tb1 && !tb2) hipLaunchKernelGGL((gemm_f32_pair<BM, BN, true, false>), dim3(grid), dim3(256), 0, s, g1, t1, g2);
+  else hipLaunchKernelGGL((gemm_f32_pair<BM, BN, true, true>), dim3(grid), dim3(256), 0, s, g1, t1, g2);
+  return hipGetLastError();
+}
+
+bool valid_args(const GemmArgs& a) {
+  // With beta != 0 the accumulators start from beta*C and op(A) is scaled by alpha,
+  // which is exact only for alpha = +-1 and beta = 1 (the only uses); 32-bit in-tile offsets.
+  if (a.beta != 0.0f && !(a.beta == 1.0f && (a.alpha == 1.0f || a.alpha == -1.0f))) return false;
+  return a.ldc < (int64_t)1 << 24 && a.lda < (int64_t)1 << 24 && a.ldb < (int64_t)1 << 24;
+}
+
+Dev make_dev(const GemmArgs& a) {
+  const int vec = aligned16(a.A) && aligned16(a.B) && !(a.lda % 4) && !(a.ldb % 4);
+  return Dev{a.M, a.N, a.K, a.A, a.lda, a.triA, a.B, a.ldb, a.triB, a.C, a.ldc, a.triC, a.alpha,
+             a.beta, vec};
+}
+
 }  // namespace
+
+hipError_t gemm_f32_pair(const GemmArgs& a1, const GemmArgs& a2, hipStream_t stream,
+                         const char* prof_name) {
+  if (a1.M <= 0 || a1.N <= 0) return gemm_f32(a2, stream, prof_name);
+  if (a2.M <= 0 || a2.N <= 0) return gemm_f32(a1, stream, prof_name);
+  if (a1.transA || a2.transA || !valid_args(a1) || !valid_args(a2)) return hipErrorInvalidValue;
+  const Dev g1 = make_dev(a1), g2 = make_dev(a2);
+  ProfScope ps(prof_name, stream);
+  const int64_t big = ceil_div(a1.M, 128) * ceil_div(a1.N, 128) + ceil_div(a2.M, 128) * ceil_div(a2.N, 128);
+  if (big >= 192) return launch_pair<128, 128>(g1, a1.transB, g2, a2.transB, stream);
+  return launch_pair<64, 64>(g1, a1.transB, g2, a2.transB, stream);
+}
 
 hipError_t gemm_f32(const GemmArgs& a, hipStream_t stream, const char* prof_name) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;

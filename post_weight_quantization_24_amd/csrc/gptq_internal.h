@@ -50,6 +50,9 @@ struct GemmArgs {
   float alpha, beta;
 };
 hipError_t gemm_f32(const GemmArgs& g, hipStream_t stream, const char* prof_name);
+// Two independent products in one launch (op(A) = A for both; transB may differ).
+hipError_t gemm_f32_pair(const GemmArgs& g1, const GemmArgs& g2, hipStream_t stream,
+                         const char* prof_name);
 
 // ---------------------------------------------------------------- prepare (prep.hip)
 size_t prepare_ws_bytes(int64_t d);

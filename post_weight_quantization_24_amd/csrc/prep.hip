@@ -6,10 +6,9 @@
 // factor.  A recursion on the 2x2 block split A = [[A11, A12], [A12^T, A22]]:
 //     G22 = factor(A22)                     (recursion)
 //     P   = A12 G22^T                       (= U12)
-//     A12 <- P G22
-//     A11 <- A11 - P P^T                    (Schur complement, upper triangle only)
+//     Q   = P G22,  A11 <- A11 - P P^T      (one launch; Schur complement, upper triangle)
 //     G11 = factor(A11)                     (recursion)
-//     G12 = -G11 (P G22) = -G11 A12
+//     G12 = -G11 Q                          (written over A12)
 // All products run on the fp32 MFMA GEMM; blocks of at most 128 are factored and
 // inverted by one workgroup in LDS.  Everything happens in the upper triangle of G;
 // the strictly lower triangle is zeroed at the end.
@@ -75,14 +74,6 @@ __global__ void __launch_bounds__(256) zero_lower(float* __restrict__ G, int64_t
   for (int64_t i = blockIdx.y; i < d; i += gridDim.y)
     for (int64_t j = blockIdx.x * 256 + threadIdx.x; j < i; j += (int64_t)gridDim.x * 256)
       G[i * d + j] = 0.0f;
-}
-
-__global__ void __launch_bounds__(256)
-copy_block(const float* __restrict__ src, int64_t lds, float* __restrict__ dst, int64_t ldd,
-           int64_t rows, int64_t cols) {
-  for (int64_t i = blockIdx.y; i < rows; i += gridDim.y)
-    for (int64_t j = blockIdx.x * 256 + threadIdx.x; j < cols; j += (int64_t)gridDim.x * 256)
-      dst[i * ldd + j] = src[i * lds + j];
 }
 
 dim3 rows_grid(int64_t rows, int64_t cols) {
@@ -343,54 +334,59 @@ leaf_factor_invert(float* __restrict__ A, int64_t ld, int64_t off, int n, int* f
   }
 }
 
-hipError_t copy2d(const float* src, int64_t lds, float* dst, int64_t ldd, int64_t rows,
-                  int64_t cols, hipStream_t s) {
-  hipLaunchKernelGGL(copy_block, rows_grid(rows, cols), dim3(256), 0, s, src, lds, dst, ldd, rows,
-                     cols);
-  return hipGetLastError();
+// Split of an n-block: the leading m columns (a multiple of the leaf size) and the rest.
+int64_t split_of(int64_t n) {
+  int64_t m = (n / 2) / NB * NB;
+  return m == 0 ? n - NB : m;
+}
+// Floats of the Q stack needed by factor_rec on an n-block (see below).
+int64_t q_stack(int64_t n) {
+  if (n <= NB) return 0;
+  const int64_t m = split_of(n), r = n - m;
+  const int64_t own = align_up((size_t)(m * r), 64);
+  const int64_t right = q_stack(r), left = own + q_stack(m);
+  return right > left ? right : left;
 }
 
-hipError_t factor_rec(float* A, int64_t ld, int64_t off, int64_t n, float* tmp, int* flag,
-                      hipStream_t s) {
+// P (m x r) is scratch shared by all nodes (it is dead once Q and the Schur update are
+// formed); Q = P G22 must survive the recursion on A11, so each node takes its Q from a
+// stack above the ones of its ancestors.
+hipError_t factor_rec(float* A, int64_t ld, int64_t off, int64_t n, float* P, float* qstack,
+                      int* flag, hipStream_t s) {
   hipError_t e;
   if (n <= NB) {
     ProfScope ps("prep_leaf", s);
     hipLaunchKernelGGL(leaf_factor_invert, dim3(1), dim3(256), 0, s, A, ld, off, (int)n, flag);
     return hipGetLastError();
   }
-  int64_t m = (n / 2) / NB * NB;
-  if (m == 0) m = n - NB;
-  const int64_t r = n - m;
+  const int64_t m = split_of(n), r = n - m;
   float* A11 = A + off * ld + off;
   float* A12 = A11 + m;
   float* A22 = A + (off + m) * ld + off + m;
+  float* Q = qstack;
 
-  if ((e = factor_rec(A, ld, off + m, r, tmp, flag, s)) != hipSuccess) return e;
+  if ((e = factor_rec(A, ld, off + m, r, P, qstack, flag, s)) != hipSuccess) return e;
   // P = A12 G22^T   (op(B)[k][j] = G22[j][k], zero for k < j)
-  if ((e = gemm_f32({m, r, r, A12, ld, 0, 0, A22, ld, 1, 2, tmp, r, 0, 1.0f, 0.0f}, s,
+  if ((e = gemm_f32({m, r, r, A12, ld, 0, 0, A22, ld, 1, 2, P, r, 0, 1.0f, 0.0f}, s,
                     "prep_gemm")) != hipSuccess)
     return e;
-  // A12 <- P G22    (G22 upper: zero for k > j)
-  if ((e = gemm_f32({m, r, r, tmp, r, 0, 0, A22, ld, 0, 1, A12, ld, 0, 1.0f, 0.0f}, s,
-                    "prep_gemm")) != hipSuccess)
+  // Q = P G22 (G22 upper: zero for k > j), and A11 <- A11 - P P^T (upper triangle)
+  if ((e = gemm_f32_pair({m, r, r, P, r, 0, 0, A22, ld, 0, 1, Q, r, 0, 1.0f, 0.0f},
+                         {m, m, r, P, r, 0, 0, P, r, 1, 0, A11, ld, 1, -1.0f, 1.0f}, s,
+                         "prep_gemm")) != hipSuccess)
     return e;
-  // A11 <- A11 - P P^T, upper triangle
-  if ((e = gemm_f32({m, m, r, tmp, r, 0, 0, tmp, r, 1, 0, A11, ld, 1, -1.0f, 1.0f}, s,
-                    "prep_gemm")) != hipSuccess)
+  if ((e = factor_rec(A, ld, off, m, P, qstack + align_up((size_t)(m * r), 64), flag, s)) !=
+      hipSuccess)
     return e;
-  if ((e = factor_rec(A, ld, off, m, tmp, flag, s)) != hipSuccess) return e;
-  // G12 = -G11 A12   (G11 upper: zero for k < i)
-  if ((e = gemm_f32({m, r, m, A11, ld, 0, 1, A12, ld, 0, 0, tmp, r, 0, -1.0f, 0.0f}, s,
-                    "prep_gemm")) != hipSuccess)
-    return e;
-  return copy2d(tmp, r, A12, ld, m, r, s);
+  // G12 = -G11 Q   (G11 upper: zero for k < i), straight into A12
+  return gemm_f32({m, r, m, A11, ld, 0, 1, Q, r, 0, 0, A12, ld, 0, -1.0f, 0.0f}, s, "prep_gemm");
 }
 
 }  // namespace
 
 size_t prepare_ws_bytes(int64_t d) {
-  const int64_t h = d / 2;
-  return 256 + (size_t)(h * (d - h) + 64) * sizeof(float);
+  const int64_t p = d > NB ? split_of(d) * (d - split_of(d)) : 0;   // largest P
+  return 256 + (align_up((size_t)p, 64) + (size_t)q_stack(d) + 64) * sizeof(float);
 }
 
 int* prepare_flag_ptr(void* ws, int64_t d) { return carve(ws, d).flag; }
@@ -406,7 +402,10 @@ hipError_t prepare_launch(const float* H, float* G, int64_t d, float damp_frac, 
     hipLaunchKernelGGL(copy_damp, rows_grid(d, d), dim3(256), 0, stream, H, G, d, w.lambda);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = factor_rec(G, d, 0, d, w.tmp, w.flag, stream)) != hipSuccess) return e;
+  const int64_t p = d > NB ? split_of(d) * (d - split_of(d)) : 0;
+  if ((e = factor_rec(G, d, 0, d, w.tmp, w.tmp + align_up((size_t)p, 64), w.flag, stream)) !=
+      hipSuccess)
+    return e;
   hipLaunchKernelGGL(zero_lower, rows_grid(d, d), dim3(256), 0, stream, G, d);
   return hipGetLastError();
 }

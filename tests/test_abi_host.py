@@ -48,7 +48,11 @@ def test_hessian_validation(lib):
 def test_prepare_validation(lib):
     f = lib.gptq_prepare_hinv
     ws = lib.gptq_prepare_workspace_size(64)
-    assert ws >= 64 * 64 // 4 * 4
+    assert ws >= 256                      # lambda and the pivot flag
+    # blocks above the leaf size need the P scratch (2048 x 2048 floats at d = 4096) and the
+    # stack of Q blocks (one per level of the left spine)
+    assert lib.gptq_prepare_workspace_size(4096) >= (2048 * 2048 + 2048 * 2048) * 4
+    assert lib.gptq_prepare_workspace_size(4096) < 4096 * 4096 * 4
     assert f(FAKE, FAKE, 0, 0.01, FAKE, ws, None, None) == G.EINVAL
     assert f(None, FAKE, 64, 0.01, FAKE, ws, None, None) == G.EINVAL
     assert f(FAKE, FAKE, 64, -0.5, FAKE, ws, None, None) == G.EINVAL
