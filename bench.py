@@ -51,6 +51,47 @@ def parse():
     return p.parse_args()
 
 
+LEAF = 128   # block size below which the inverse factor is done by one workgroup
+
+
+def prep_gemm_flops(n):
+    """Useful flops of the products of the inverse-factor recursion on an n-block: for the
+    split n = m + r, P = A12 G22^T and Q = P G22 (m r (r+1) each, triangular G22), the
+    Schur update A11 -= P P^T (upper triangle, m (m+1) r) and G12 = -G11 Q (m (m+1) r)."""
+    if n <= LEAF:
+        return 0
+    m = (n // 2) // LEAF * LEAF or n - LEAF
+    r = n - m
+    return 2 * m * r * (r + 1) + 2 * m * (m + 1) * r + prep_gemm_flops(m) + prep_gemm_flops(r)
+
+
+def leaf_sizes(n):
+    if n <= LEAF:
+        return [n]
+    m = (n // 2) // LEAF * LEAF or n - LEAF
+    return leaf_sizes(m) + leaf_sizes(n - m)
+
+
+def family_work(fam, d_row, d_col, n_tok, bits, block, x_dtype):
+    """Algorithmic work of one step for a kernel family: (amount, unit, peak, bound)."""
+    f32, f16, hbm = PEAK["mfma_f32"], PEAK["mfma_f16"], PEAK["hbm"]
+    if fam == "hessian_mfma":      # the d (d + 1) / 2 distinct entries, 2 flops per token each
+        return n_tok * d_col * (d_col + 1), "TFLOP/s", f16 if x_dtype == "f16" else f32, "mfma"
+    if fam == "prep_gemm":
+        return prep_gemm_flops(d_col), "TFLOP/s", f32, "mfma"
+    if fam == "prep_leaf":         # factor and invert: n^3 / 3 flops each
+        return sum(2 * n ** 3 // 3 for n in leaf_sizes(d_col)), "TFLOP/s", f32, "mfma"
+    if fam == "lazy_gemm":         # sum over blocks of 2 d_row B (d_col - j - B)
+        return d_row * d_col * (d_col - block), "TFLOP/s", f32, "mfma"
+    if fam == "quant_block":       # read W, write E and codes, read the G blocks
+        return d_row * d_col * (8 + bits / 8) + d_col * block * 4, "GB/s", hbm, "hbm"
+    if fam == "quant_convert":
+        return d_row * d_col * 6, "GB/s", hbm, "hbm"
+    if fam == "hessian_reduce":    # H read and written (the partial tiles are extra)
+        return d_col * d_col * 8, "GB/s", hbm, "hbm"
+    return d_col * d_col * 8, "GB/s", hbm, "hbm"
+
+
 KERNEL_SOURCE = {   # kernel family -> the source file its counters were taken from
     "hessian_mfma": "hessian.hip", "hessian_reduce": "hessian.hip", "prep_leaf": "prep.hip",
     "prep_gemm": "gemm.hip", "lazy_gemm": "gemm.hip", "quant_block": "quant.hip",
@@ -226,21 +267,13 @@ def main():
     timed = read_phases(a.steps)[dom]
     avg_s = timed["avg_launch_ms"] / 1e3
     launches_per_step = timed["launches_per_step"]
-    # algorithmic work per launch of each family
-    if dom == "hessian_mfma":
-        work, unit, peak, bound = n_tok * d_col * (d_col + 1), "TFLOP/s", PEAK["mfma_f16"], "mfma"
-        achieved = work / avg_s / 1e12
-    elif dom == "lazy_gemm":
-        per = d_row * d_col * (d_col - block) / launches_per_step
-        work, unit, peak, bound = per, "TFLOP/s", PEAK["mfma_f32"], "mfma"
-        achieved = work / avg_s / 1e12
-    else:
-        work, unit, peak, bound = None, "TFLOP/s", PEAK["mfma_f32"], "mfma"
-        achieved = 0.0
+    work, unit, peak, bound = family_work(dom, d_row, d_col, n_tok, bits, block, wl.dtype)
+    achieved = work / launches_per_step / avg_s / (1e12 if unit == "TFLOP/s" else 1e9)
     traffic = kernel_traffic(a.traffic, dom, workload=wl.name, layer=layer.name, bits=bits,
                              block=block)
     roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-                "frac": achieved / peak, "traffic": traffic, "kernel": dom}
+                "frac": achieved / peak, "traffic": traffic, "kernel": dom,
+                "work_per_launch": work / launches_per_step}
 
     cpu = None
     if not a.no_cpu:
