@@ -44,6 +44,7 @@ __global__ void __launch_bounds__(256) zero_f64(double* __restrict__ p, int64_t 
 struct Params {
   float s;
   float z;
+  float y;   // RN(1/s): w/s is formed as RN(q0 + RN(w - q0 s) y) with q0 = RN(w y)
 };
 
 // (s, z) from the group's min and max (already including 0 for the asymmetric form).
@@ -65,7 +66,19 @@ __device__ __forceinline__ Params make_params(float mn, float mx, int bits, int 
     const float zf = __fdiv_rn(-lo, p.s);
     p.z = fminf(fmaxf(__builtin_rintf(zf), 0.0f), (float)maxq);
   }
+  p.y = __fdiv_rn(1.0f, p.s);
   return p;
+}
+
+// w / s correctly rounded (the same value as an IEEE division) from the correctly rounded
+// reciprocal y: q0 = RN(w y) is within an ulp of w / s, r = w - q0 s is exact with an FMA,
+// and one correction RN(q0 + r y) then gives RN(w / s) (Markstein's theorem on division
+// with a correctly rounded reciprocal; also checked against exact rational arithmetic).
+// Three dependent operations instead of the eleven of a general division.
+__device__ __forceinline__ float div_by_scale(float w, const Params& p) {
+  const float q0 = w * p.y;
+  const float r = fmaf(-q0, p.s, w);
+  return fmaf(r, p.y, q0);
 }
 
 // One wave per row: parameters of the group [c0, c0 + g) from the current weights.
@@ -106,6 +119,12 @@ __device__ __forceinline__ float row_min(float v) {
   v = fminf(v, dpp<0x122>(v));
   return fminf(v, dpp<0x121>(v));
 }
+__device__ __forceinline__ float row_sum(float v) {
+  v += dpp<0x128>(v);
+  v += dpp<0x124>(v);
+  v += dpp<0x122>(v);
+  return v + dpp<0x121>(v);
+}
 __device__ __forceinline__ float row_max(float v) {
   v = fmaxf(v, dpp<0x128>(v));
   v = fmaxf(v, dpp<0x124>(v));
@@ -126,22 +145,38 @@ constexpr int g_lds_floats() { return grow_off<B>(B); }
 template <int B>
 struct Row {
   static constexpr int S = B / LPR;
-  float w[S];      // current weights of the owned columns
+  float w[S];      // current weights of the owned columns (column s*16 + lane)
+  float code[S];   // decided codes of the owned columns
+  float err[S];    // e of the owned columns, for the lazy update
+  float gc[S];     // G_qk / G_qq of the current column q for the owned columns k
+  float gn[S];     // the same for the next column (read one step ahead)
   Params p;
-  float esq;
 };
 
 template <int B, int Q>
-__device__ __forceinline__ void quant_step(Row<B>& r, const float* __restrict__ gl,
-                                           const float* __restrict__ rinv, int c, int bits,
+__device__ __forceinline__ void load_coef(Row<B>& r, const float* gl, int c) {
+  constexpr int S = B / LPR;
+  constexpr int A = Q / LPR;
+  const float* gq = gl + grow_off<B>(Q);
+#pragma unroll
+  for (int s = A; s < S; ++s) r.gn[s] = gq[(s - A) * LPR + c];
+}
+
+template <int B, int Q>
+__device__ __forceinline__ void quant_step(Row<B>& r, const float* gl, int c, int bits,
                                            int sym, int64_t g, int width, int64_t j0,
                                            float* __restrict__ scales, uint8_t* __restrict__ zeros,
-                                           int64_t n_groups, int64_t row, bool row_ok,
-                                           uint8_t* __restrict__ crow, float* __restrict__ erow) {
+                                           int64_t n_groups, int64_t row, bool row_ok) {
   constexpr int S = B / LPR;
   constexpr int A = Q / LPR;   // slot holding column Q
   constexpr int O = Q % LPR;   // owner lane
   const int maxq = (1 << bits) - 1;
+  // this column's coefficients were read during the previous step; read the next ones now
+#pragma unroll
+  for (int s = A; s < S; ++s) r.gc[s] = r.gn[s];
+  if (Q + 1 < B) load_coef<B, (Q + 1 < B ? Q + 1 : Q)>(r, gl, c);
+  // keep later steps' LDS reads from being hoisted here (they would each hold a register)
+  __asm__ volatile("" ::: "memory");
   // groups are multiples of 16 columns, so a group can only start at a multiple of 16
   if (O == 0 && g <= B && (Q % g) == 0 && Q < width) {
     // group [Q, Q + g) inside the block: min / max of the current values
@@ -164,32 +199,27 @@ __device__ __forceinline__ void quant_step(Row<B>& r, const float* __restrict__ 
     }
   }
   const float x = r.w[A];
-  const float v = __fdiv_rn(x, r.p.s) + r.p.z;
+  const float v = div_by_scale(x, r.p) + r.p.z;
   const float code = fminf(fmaxf(__builtin_rintf(v), 0.0f), (float)maxq);
   const float wq = r.p.s * (code - r.p.z);
-  float e = (x - wq) * rinv[Q];
-  e = dpp<0x150 + O>(e);  // row_newbcast: every lane of the row takes the owner's e
-  if (Q >= width) e = 0.0f;
-  if (c == O) {
-    crow[Q] = (uint8_t)code;       // LDS, packed after the block
-    if (row_ok) erow[Q] = e;       // E for the lazy update
+  // d = w - w^ (e = d / G_qq is formed after the block; the stored G rows carry the 1/G_qq)
+  float dq = dpp<0x150 + O>(x - wq);  // row_newbcast: every lane takes the owner's d
+  if (Q >= width) dq = 0.0f;
+  if (c == O) {            // register selects, no memory traffic on the column chain
+    r.code[A] = code;
+    r.err[A] = dq;
   }
-  r.esq = fmaf(e, e, r.esq);
-  const float* gq = gl + grow_off<B>(Q);
 #pragma unroll
-  for (int s = A; s < S; ++s) r.w[s] = fmaf(-e, gq[(s - A) * LPR + c], r.w[s]);
-  // keep later steps' LDS loads from being hoisted here (they would each hold a register)
-  __asm__ volatile("" ::: "memory");
+  for (int s = A; s < S; ++s) r.w[s] = fmaf(-dq, r.gc[s], r.w[s]);
 }
 
 template <int B, int... Qs>
-__device__ __forceinline__ void quant_steps(Row<B>& r, const float* gl, const float* rinv, int c,
+__device__ __forceinline__ void quant_steps(Row<B>& r, const float* gl, int c,
                                             int bits, int sym, int64_t g, int width, int64_t j0,
                                             float* scales, uint8_t* zeros, int64_t n_groups,
-                                            int64_t row, bool row_ok, uint8_t* crow, float* erow,
+                                            int64_t row, bool row_ok,
                                             std::integer_sequence<int, Qs...>) {
-  (quant_step<B, Qs>(r, gl, rinv, c, bits, sym, g, width, j0, scales, zeros, n_groups, row,
-                     row_ok, crow, erow),
+  (quant_step<B, Qs>(r, gl, c, bits, sym, g, width, j0, scales, zeros, n_groups, row, row_ok),
    ...);
 }
 
@@ -205,15 +235,16 @@ quant_block(const float* __restrict__ Wc, const float* __restrict__ G, int64_t d
   float* rinv = smem + g_lds_floats<B>();    // 1 / G_qq
   uint8_t* cbuf = reinterpret_cast<uint8_t*>(rinv + B);  // codes [ROWS_PER_WG][B]
 
-  // stage G[j0 + q][j0 + s*16 + c] for columns > q (0 elsewhere)
+  // stage G[j0 + q][j0 + s*16 + c] / G_qq for columns > q (0 elsewhere)
   for (int q = threadIdx.x / LPR; q < B; q += 256 / LPR) {
     const int c = threadIdx.x % LPR;
     const int a = q / LPR;
     float* dst = gl + grow_off<B>(q);
+    const float rq = q < width ? 1.0f / G[(j0 + q) * d_col + j0 + q] : 0.0f;
     for (int s = a; s < S; ++s) {
       const int k = s * LPR + c;
       dst[(s - a) * LPR + c] =
-          (k > q && k < width && q < width) ? G[(j0 + q) * d_col + j0 + k] : 0.0f;
+          (k > q && k < width && q < width) ? G[(j0 + q) * d_col + j0 + k] * rq : 0.0f;
     }
   }
   for (int q = threadIdx.x; q < B; q += 256)
@@ -229,22 +260,43 @@ quant_block(const float* __restrict__ Wc, const float* __restrict__ G, int64_t d
     const int k = s * LPR + c;
     r.w[s] = (row_ok && k < width) ? Wc[row * d_col + j0 + k] : 0.0f;
   }
-  r.esq = 0.0f;
   if (g > B) {
     const int64_t gi = j0 / g;
-    r.p.s = row_ok ? scales[row * n_groups + gi] : 1.0f;
+    const float sc = row_ok ? scales[row * n_groups + gi] : 1.0f;
+    r.p.s = sc;
     r.p.z = row_ok ? (float)zeros[row * n_groups + gi] : 0.0f;
+    r.p.y = __fdiv_rn(1.0f, sc);
   } else {
     r.p.s = 1.0f;
     r.p.z = 0.0f;
+    r.p.y = 1.0f;
+  }
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    r.code[s] = 0.0f;
+    r.err[s] = 0.0f;
   }
   __syncthreads();
+  load_coef<B, 0>(r, gl, c);
 
-  quant_steps<B>(r, gl, rinv, c, bits, sym, g, width, j0, scales, zeros, n_groups, row, row_ok,
-                 cbuf + rl * B, E + (row_ok ? row : 0) * d_col + j0,
+  quant_steps<B>(r, gl, c, bits, sym, g, width, j0, scales, zeros, n_groups, row, row_ok,
                  std::make_integer_sequence<int, B>{});
 
-  if (row_ok && c == 0 && err_sq) err_sq[row] += (double)r.esq;
+  // codes of the owned columns to LDS (for packing); e = d / G_qq to E (16 lanes per 64
+  // bytes) and its squares summed over the row
+  uint8_t* crow = cbuf + rl * B;
+  float* erow = E + (row_ok ? row : 0) * d_col + j0;
+  float esq = 0.0f;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int k = s * LPR + c;
+    crow[k] = (uint8_t)r.code[s];
+    const float e = r.err[s] * rinv[k];
+    esq = fmaf(e, e, esq);
+    if (row_ok && k < width) erow[k] = e;
+  }
+  esq = row_sum(esq);
+  if (row_ok && c == 0 && err_sq) err_sq[row] += (double)esq;
   // pack: each lane assembles whole 32-bit words from the row's code bytes in LDS
   __syncthreads();
   if (row_ok) {
