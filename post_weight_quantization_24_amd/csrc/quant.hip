@@ -146,7 +146,7 @@ template <int B>
 struct Row {
   static constexpr int S = B / LPR;
   float w[S];      // current weights of the owned columns (column s*16 + lane)
-  float code[S];   // decided codes of the owned columns
+  uint32_t code[(S + 3) / 4];   // decided codes of the owned columns, one byte each
   float err[S];    // e of the owned columns, for the lazy update
   float gc[S];     // G_qk / G_qq of the current column q for the owned columns k
   float gn[S];     // the same for the next column (read one step ahead)
@@ -206,7 +206,8 @@ __device__ __forceinline__ void quant_step(Row<B>& r, const float* gl, int c, in
   float dq = dpp<0x150 + O>(x - wq);  // row_newbcast: every lane takes the owner's d
   if (Q >= width) dq = 0.0f;
   if (c == O) {            // register selects, no memory traffic on the column chain
-    r.code[A] = code;
+    constexpr int SH = 8 * (A % 4);
+    r.code[A / 4] = (r.code[A / 4] & ~(0xffu << SH)) | ((uint32_t)code << SH);
     r.err[A] = dq;
   }
 #pragma unroll
@@ -235,20 +236,37 @@ quant_block(const float* __restrict__ Wc, const float* __restrict__ G, int64_t d
   float* rinv = smem + g_lds_floats<B>();    // 1 / G_qq
   uint8_t* cbuf = reinterpret_cast<uint8_t*>(rinv + B);  // codes [ROWS_PER_WG][B]
 
-  // stage G[j0 + q][j0 + s*16 + c] / G_qq for columns > q (0 elsewhere)
-  for (int q = threadIdx.x / LPR; q < B; q += 256 / LPR) {
-    const int c = threadIdx.x % LPR;
-    const int a = q / LPR;
-    float* dst = gl + grow_off<B>(q);
-    const float rq = q < width ? 1.0f / G[(j0 + q) * d_col + j0 + q] : 0.0f;
-    for (int s = a; s < S; ++s) {
-      const int k = s * LPR + c;
-      dst[(s - a) * LPR + c] =
-          (k > q && k < width && q < width) ? G[(j0 + q) * d_col + j0 + k] * rq : 0.0f;
-    }
-  }
+  // Stage G[j0 + q][j0 + s*16 + c] / G_qq for columns > q (0 elsewhere).  Thread (q0, c)
+  // handles rows q = q0 + 16 i; row q keeps slots i..S-1, so every index is known at
+  // compile time and the loads of up to four rows are in flight together.
   for (int q = threadIdx.x; q < B; q += 256)
     rinv[q] = q < width ? 1.0f / G[(j0 + q) * d_col + j0 + q] : 0.0f;
+  __syncthreads();
+  {
+    const int q0 = threadIdx.x / LPR, c = threadIdx.x % LPR;
+    const float* gsrc = G + (j0 + q0) * d_col + j0 + c;
+    constexpr int RPC = S < 4 ? S : (S > 8 ? 2 : 4);   // rows per chunk (bounded registers)
+#pragma unroll
+    for (int i0 = 0; i0 < S; i0 += RPC) {
+      float v[RPC][S];
+#pragma unroll
+      for (int i = i0; i < i0 + RPC; ++i)
+#pragma unroll
+        for (int s = i; s < S; ++s) {
+          const int q = q0 + LPR * i, k = s * LPR + c;
+          v[i - i0][s] = (k > q && k < width && q < width)
+                             ? gsrc[(int64_t)LPR * i * d_col + s * LPR] : 0.0f;
+        }
+#pragma unroll
+      for (int i = i0; i < i0 + RPC; ++i) {
+        const int q = q0 + LPR * i;
+        const float rq = rinv[q];
+        float* dst = gl + grow_off<B>(q);
+#pragma unroll
+        for (int s = i; s < S; ++s) dst[(s - i) * LPR + c] = v[i - i0][s] * rq;
+      }
+    }
+  }
 
   const int c = threadIdx.x % LPR;
   const int rl = threadIdx.x / LPR;  // row within the workgroup
@@ -272,10 +290,9 @@ quant_block(const float* __restrict__ Wc, const float* __restrict__ G, int64_t d
     r.p.y = 1.0f;
   }
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
-    r.code[s] = 0.0f;
-    r.err[s] = 0.0f;
-  }
+  for (int s = 0; s < S; ++s) r.err[s] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < (S + 3) / 4; ++s) r.code[s] = 0u;
   __syncthreads();
   load_coef<B, 0>(r, gl, c);
 
@@ -290,7 +307,7 @@ quant_block(const float* __restrict__ Wc, const float* __restrict__ G, int64_t d
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int k = s * LPR + c;
-    crow[k] = (uint8_t)r.code[s];
+    crow[k] = (uint8_t)(r.code[s / 4] >> (8 * (s % 4)));
     const float e = r.err[s] * rinv[k];
     esq = fmaf(e, e, esq);
     if (row_ok && k < width) erow[k] = e;
