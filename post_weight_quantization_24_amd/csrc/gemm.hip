@@ -26,8 +26,28 @@ struct Dev {
   const float* B; int64_t ldb; int triB;
   float* C; int64_t ldc; int triC;
   float alpha, beta;
-  int vec;   // operands and leading dimensions allow 16-byte loads
+  int vec;     // operands and leading dimensions allow 16-byte loads
+  int order;   // tile order: 0 by rows, 1 by columns, 2 by columns from the last, 3 by rows
+               // from the last (a triangular mask makes K per tile vary; long tiles first)
 };
+
+// Output tile `tile` of the launch -> tile coordinates, in the order `order`.
+__device__ __forceinline__ void tile_origin(const Dev& g, int64_t tile, int BM, int BN, int64_t& m0,
+                                            int64_t& n0) {
+  const int64_t tm = (g.M + BM - 1) / BM, tn = (g.N + BN - 1) / BN;
+  int64_t i, j;
+  if (g.order == 1 || g.order == 2) {
+    i = tile % tm;
+    j = tile / tm;
+    if (g.order == 2) j = tn - 1 - j;
+  } else {
+    i = tile / tn;
+    j = tile % tn;
+    if (g.order == 3) i = tm - 1 - i;
+  }
+  m0 = i * BM;
+  n0 = j * BN;
+}
 
 template <int BM, int BN, bool TA, bool TB>
 struct Cfg {
@@ -83,9 +103,8 @@ __device__ __forceinline__ void gemm_tile(const Dev& g, int64_t tile, Smem<BM, B
   auto& As = sm.a;
   auto& Bs = sm.b;
 
-  const int64_t tiles_n = (g.N + BN - 1) / BN;
-  const int64_t m0 = (int64_t)(tile / tiles_n) * BM;
-  const int64_t n0 = (int64_t)(tile % tiles_n) * BN;
+  int64_t m0, n0;
+  tile_origin(g, tile, BM, BN, m0, n0);
   if (g.triC == 1 && m0 >= n0 + BN) return;  // tile entirely below the diagonal
 
   int64_t k_lo = 0, k_hi = g.K;
@@ -350,9 +369,8 @@ __global__ void __launch_bounds__(256, 2) gemm_f32_dma(Dev g) {
   using C = DCfg<BM, BN, TB>;
   __shared__ __attribute__((aligned(1024))) char ring[DNS * C::STAGE];
 
-  const int64_t tiles_n = (g.N + BN - 1) / BN;
-  const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * BM;
-  const int64_t n0 = (int64_t)(blockIdx.x % tiles_n) * BN;
+  int64_t m0, n0;
+  tile_origin(g, blockIdx.x, BM, BN, m0, n0);
   if (g.triC == 1 && m0 >= n0 + BN) return;  // tile entirely below the diagonal
 
   int64_t k_lo = 0, k_hi = g.K;
@@ -531,10 +549,19 @@ bool valid_args(const GemmArgs& a) {
   return a.ldc < (int64_t)1 << 24 && a.lda < (int64_t)1 << 24 && a.ldb < (int64_t)1 << 24;
 }
 
+// Longest tiles first: K per tile shrinks with the column for a lower op(B) (k >= n),
+// grows with it for an upper op(B) (k <= n), shrinks with the row for an upper op(A).
+int tile_order(const GemmArgs& a) {
+  if (a.triB == 2) return 1;
+  if (a.triB == 1) return 2;
+  if (a.triA == 2) return 3;
+  return 0;
+}
+
 Dev make_dev(const GemmArgs& a) {
   const int vec = aligned16(a.A) && aligned16(a.B) && !(a.lda % 4) && !(a.ldb % 4);
   return Dev{a.M, a.N, a.K, a.A, a.lda, a.triA, a.B, a.ldb, a.triB, a.C, a.ldc, a.triC, a.alpha,
-             a.beta, vec};
+             a.beta, vec, tile_order(a)};
 }
 
 }  // namespace
@@ -547,7 +574,8 @@ hipError_t gemm_f32_pair(const GemmArgs& a1, const GemmArgs& a2, hipStream_t str
   const Dev g1 = make_dev(a1), g2 = make_dev(a2);
   ProfScope ps(prof_name, stream);
   const int64_t big = ceil_div(a1.M, 128) * ceil_div(a1.N, 128) + ceil_div(a2.M, 128) * ceil_div(a2.N, 128);
-  if (big >= 192) return launch_pair<128, 128>(g1, a1.transB, g2, a2.transB, stream);
+  const bool masked = a1.triA || a1.triB || a1.triC || a2.triA || a2.triB || a2.triC;
+  if (!masked && big >= 192) return launch_pair<128, 128>(g1, a1.transB, g2, a2.transB, stream);
   return launch_pair<64, 64>(g1, a1.transB, g2, a2.transB, stream);
 }
 
@@ -561,11 +589,13 @@ hipError_t gemm_f32(const GemmArgs& a, hipStream_t stream, const char* prof_name
   // (otherwise every step takes the element-wise path).
   if (a.ldc >= (int64_t)1 << 24 || a.lda >= (int64_t)1 << 24 || a.ldb >= (int64_t)1 << 24)
     return hipErrorInvalidValue;
-  const int vec = aligned16(a.A) && aligned16(a.B) && !(a.lda % 4) && !(a.ldb % 4);
-  Dev g{a.M, a.N, a.K, a.A, a.lda, a.triA, a.B, a.ldb, a.triB, a.C, a.ldc, a.triC, a.alpha, a.beta,
-        vec};
+  const Dev g = make_dev(a);
+  const int vec = g.vec;
   ProfScope ps(prof_name, stream);
   const int64_t big_tiles = ceil_div(a.M, 128) * ceil_div(a.N, 128);
+  // With a triangular mask K differs per tile: 64 x 64 tiles, longest first, let the
+  // dispatcher balance the CUs (one 128 x 128 tile per CU would wait for the longest).
+  const bool masked = a.triA || a.triB || a.triC;
   // direct-to-LDS path: A row-major, 16-byte rows and chunks that do not straddle an edge
   // (byte offsets inside a 128-row tile stay below 2^31 for leading dimensions < 2^21)
   const bool dma = vec && !a.transA && a.K % 4 == 0 && a.K >= 4 && (a.transB || a.N % 4 == 0) &&
@@ -574,8 +604,9 @@ hipError_t gemm_f32(const GemmArgs& a, hipStream_t stream, const char* prof_name
   // Measured on MI355X: the direct-to-LDS kernel only wins for long K on large outputs
   // (4096 x 2048 x 2048: 97 vs 91 TFLOP/s); for shorter K or fewer tiles the register-staged
   // kernel is as fast or faster (e.g. 1024^3: 61 vs 48 TFLOP/s).
-  if (dma && big_tiles >= 256 && a.K >= 2048) return launch_dma<128, 128>(g, a.transB, stream);
-  if (big_tiles >= 192) return launch<128, 128>(g, a.transA, a.transB, stream);
+  if (!masked && dma && big_tiles >= 256 && a.K >= 2048)
+    return launch_dma<128, 128>(g, a.transB, stream);
+  if (!masked && big_tiles >= 192) return launch<128, 128>(g, a.transA, a.transB, stream);
   return launch<64, 64>(g, a.transA, a.transB, stream);
 }
 
