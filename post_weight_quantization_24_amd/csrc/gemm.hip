@@ -574,7 +574,8 @@ hipError_t gemm_f32_pair(const GemmArgs& a1, const GemmArgs& a2, hipStream_t str
   const Dev g1 = make_dev(a1), g2 = make_dev(a2);
   ProfScope ps(prof_name, stream);
   const int64_t big = ceil_div(a1.M, 128) * ceil_div(a1.N, 128) + ceil_div(a2.M, 128) * ceil_div(a2.N, 128);
-  const bool masked = a1.triA || a1.triB || a1.triC || a2.triA || a2.triB || a2.triC;
+  const bool masked = (a1.triA || a1.triB || a1.triC || a2.triA || a2.triB || a2.triC) &&
+                      big < 1024;
   if (!masked && big >= 192) return launch_pair<128, 128>(g1, a1.transB, g2, a2.transB, stream);
   return launch_pair<64, 64>(g1, a1.transB, g2, a2.transB, stream);
 }
@@ -593,9 +594,10 @@ hipError_t gemm_f32(const GemmArgs& a, hipStream_t stream, const char* prof_name
   const int vec = g.vec;
   ProfScope ps(prof_name, stream);
   const int64_t big_tiles = ceil_div(a.M, 128) * ceil_div(a.N, 128);
-  // With a triangular mask K differs per tile: 64 x 64 tiles, longest first, let the
-  // dispatcher balance the CUs (one 128 x 128 tile per CU would wait for the longest).
-  const bool masked = a.triA || a.triB || a.triC;
+  // With a triangular mask K differs per tile: while there are few 128 x 128 tiles per CU
+  // (one would wait for the longest), 64 x 64 tiles, longest first, let the dispatcher
+  // balance the CUs; with many tiles per CU the larger tiles are more efficient.
+  const bool masked = (a.triA || a.triB || a.triC) && big_tiles < 1024;
   // direct-to-LDS path: A row-major, 16-byte rows and chunks that do not straddle an edge
   // (byte offsets inside a 128-row tile stay below 2^31 for leading dimensions < 2^21)
   const bool dma = vec && !a.transA && a.K % 4 == 0 && a.K >= 4 && (a.transB || a.N % 4 == 0) &&
