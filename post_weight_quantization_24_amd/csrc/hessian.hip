@@ -312,15 +312,35 @@ hess_reduce(const float* __restrict__ part, int splits, int tiles, int64_t d,
   const int64_t c0 = (int64_t)tj * TILE + sbk * 64;
   const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
   const bool diag = (r0 == c0);
-  for (int rr = ty; rr < 64; rr += 4) {
-    float v = 0.0f;
-    const int64_t off = (int64_t)(sa * 64 + rr) * TILE + sbk * 64 + tx;
-    for (int sp = 0; sp < splits; ++sp)
-      v += part[((int64_t)sp * tiles + tile) * (int64_t)TILE * TILE + off];
-    v *= 2.0f;
-    s[rr][tx] = v;
-    const int64_t i = r0 + rr, j = c0 + tx;
-    if (i < d && j < d && (!diag || j <= i)) H[i * d + j] += v;
+  const int64_t sstride = (int64_t)tiles * TILE * TILE;   // between the splits of one tile
+  const float* pt = part + (int64_t)tile * TILE * TILE + (int64_t)(sa * 64) * TILE + sbk * 64 + tx;
+  // four rows (ty + 16 q) and four splits per step: 16 loads in flight per lane; each row's
+  // sum keeps split order
+  for (int rb = ty; rb < 16; rb += 4) {
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int sp = 0;
+    for (; sp + 4 <= splits; sp += 4) {
+      float a[4][4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) a[q][k] = pt[(rb + 16 * q) * TILE + (sp + k) * sstride];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[q] += a[q][k];
+    }
+    for (; sp < splits; ++sp)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] += pt[(rb + 16 * q) * TILE + sp * sstride];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rr = rb + 16 * q;
+      const float w = 2.0f * v[q];
+      s[rr][tx] = w;
+      const int64_t i = r0 + rr, j = c0 + tx;
+      if (i < d && j < d && (!diag || j <= i)) H[i * d + j] += w;
+    }
   }
   __syncthreads();
   // mirror: H[c0 + rr][r0 + tx] += s[tx][rr] for entries strictly below the diagonal
@@ -350,10 +370,12 @@ HessPlan hessian_plan(int64_t d, int64_t n_tok, int64_t ldx, int x_dtype) {
   // one split's rows must stay below 2^30 bytes (32-bit buffer offsets)
   const int64_t elt = x_dtype == 0 ? 2 : 4;
   const int64_t min_split = ceil_div(n_tok * ldx * elt, (int64_t)1 << 30);
+  // Any split count is allowed: multiples of 8 give each XCD whole token ranges (see
+  // hess_work), other counts run split-major over all XCDs.  The measured difference between
+  // the two mappings is small; what matters is the number of full rounds of workgroups
+  // (136 tiles x 16 splits leaves a half-empty ninth round, 15 splits fill exactly eight).
   for (int64_t s = min_split; s <= max_split || s == min_split; ++s) {
     if (s > 64 && s > min_split) break;
-    // f16: multiples of 8 splits give each XCD whole token ranges (see hess_work)
-    if (x_dtype == 0 && s >= 8 && s % 8 != 0 && s != min_split) continue;
     const int64_t wgs = p.tiles * s * (x_dtype == 0 ? 1 : 16);
     const double rounds = (x_dtype == 0 && s % 8 == 0)
                               ? (double)ceil_div(p.tiles * (s / 8), cus / 8)
