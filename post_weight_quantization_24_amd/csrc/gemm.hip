@@ -13,6 +13,9 @@
 // matrix edge or a triangular mask take the per-element masked path.
 // With beta = 1 the C tile is loaded into the accumulators before the K loop and alpha
 // (+1 or -1) is folded into op(A) as it is staged, so the epilogue is a plain store.
+// Products with at most one 64 x 64 tile per CU go to a short-K kernel instead (32 x 32
+// tiles, K split over the four waves of a workgroup); long-K products with many 128 x 128
+// tiles to a direct-to-LDS variant.
 
 #include "gptq_internal.h"
 
@@ -364,13 +367,25 @@ __device__ __forceinline__ void copy_nc(rsrc_t rsrc, uint32_t lds, int q, int la
   dma16(rsrc, lds + q * (1024 + nc_pad(W)), (k * ld + n) * 4);
 }
 
-template <int BM, int BN, bool TB>
-__global__ void __launch_bounds__(256, 2) gemm_f32_dma(Dev g) {
+// vmcnt wait that leaves `later` stages of CPW copies each in flight (later <= I)
+template <int CPW, int I>
+__device__ __forceinline__ void wait_later(int later) {
+  if constexpr (I == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (later >= I) wait_vmcnt<I * CPW>();
+    else wait_later<CPW, I - 1>(later);
+  }
+}
+
+// Output tile `tile` of one problem through a ring of NS stages (NS - 1 in flight).
+template <int BM, int BN, bool TB, int NS>
+__device__ __forceinline__ void dma_tile(const Dev& g, int64_t tile, char* ring) {
   using C = DCfg<BM, BN, TB>;
-  __shared__ __attribute__((aligned(1024))) char ring[DNS * C::STAGE];
+  static_assert((NS - 2) * C::CPW <= 63, "vmcnt range");
 
   int64_t m0, n0;
-  tile_origin(g, blockIdx.x, BM, BN, m0, n0);
+  tile_origin(g, tile, BM, BN, m0, n0);
   if (g.triC == 1 && m0 >= n0 + BN) return;  // tile entirely below the diagonal
 
   int64_t k_lo = 0, k_hi = g.K;
@@ -393,7 +408,7 @@ __global__ void __launch_bounds__(256, 2) gemm_f32_dma(Dev g) {
   auto issue = [&](int st) {
     const int64_t k0 = k_lo + (int64_t)st * DBK;
     const int k_lim = (int)(g.K - k0 < DBK ? g.K - k0 : DBK);
-    const uint32_t sa = ring0 + (st % DNS) * C::STAGE, sb = sa + C::A_BYTES;
+    const uint32_t sa = ring0 + (st % NS) * C::STAGE, sb = sa + C::A_BYTES;
     const rsrc_t ra = make_rsrc(g.A + m0 * g.lda + k0);
     const rsrc_t rb = make_rsrc(TB ? g.B + n0 * g.ldb + k0 : g.B + k0 * g.ldb + n0);
 #pragma unroll
@@ -427,17 +442,15 @@ __global__ void __launch_bounds__(256, 2) gemm_f32_dma(Dev g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.0f;
 
-  if (nsteps > 0) issue(0);
-  if (nsteps > 1) issue(1);
-  if (nsteps > 2) issue(2);
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (i < nsteps) issue(i);
   for (int s = 0; s < nsteps; ++s) {
-    const int later = nsteps - 1 - s < 2 ? nsteps - 1 - s : 2;
-    if (later == 2) wait_vmcnt<2 * C::CPW>();
-    else if (later == 1) wait_vmcnt<C::CPW>();
-    else wait_vmcnt<0>();
+    const int later = nsteps - 1 - s < NS - 2 ? nsteps - 1 - s : NS - 2;
+    wait_later<C::CPW, NS - 2>(later);
     stage_barrier();
-    if (s + 3 < nsteps) issue(s + 3);   // into the buffer read in iteration s - 1
-    const char* sa = ring + (s % DNS) * C::STAGE;
+    if (s + NS - 1 < nsteps) issue(s + NS - 1);   // into the buffer read in iteration s - 1
+    const char* sa = ring + (s % NS) * C::STAGE;
     const char* sb = sa + C::A_BYTES;
     const int64_t k0 = k_lo + (int64_t)s * DBK;
     const bool msk = masked(s);
@@ -511,6 +524,128 @@ __global__ void __launch_bounds__(256, 2) gemm_f32_dma(Dev g) {
       }
 }
 
+template <int BM, int BN, bool TB, int NS>
+__global__ void __launch_bounds__(256, 2) gemm_f32_dma(Dev g) {
+  __shared__ __attribute__((aligned(1024))) char ring[NS * DCfg<BM, BN, TB>::STAGE];
+  dma_tile<BM, BN, TB, NS>(g, blockIdx.x, ring);
+}
+
+// ---------------------------------------------------------------------------------
+// Short-K products (K up to a few hundred): one workgroup per 32 x 32 output tile, the four
+// waves split K (wave w takes the 32-wide chunks w, w + 4, ...), operands go straight from
+// global memory into the MFMA registers and the four partial tiles are summed in LDS in wave
+// order.  A product of this shape is bound by the length of one wave's MFMA chain, not by
+// memory, so spreading K over more waves is what shortens it.
+// MFMA k slots: within a chunk at k0, lane half h and step i use k = k0 + 16 h + i, so a
+// lane reads 16 consecutive k of its row of A (and of B's row when B is stored N x K).
+// Loads use addresses clamped into the operands; masked or out-of-range values are zeroed.
+constexpr int SK_T = 32;   // output tile edge
+constexpr int SK_C = 32;   // k per chunk
+
+template <bool TB>
+__device__ __forceinline__ void small_tile(const Dev& g, int64_t tile, float* red) {
+  int64_t m0, n0;
+  tile_origin(g, tile, SK_T, SK_T, m0, n0);
+  if (g.triC == 1 && m0 >= n0 + SK_T) return;   // the whole workgroup leaves together
+
+  int64_t k_lo = 0, k_hi = g.K;
+  if (g.triA == 1) k_lo = m0;
+  if (g.triA == 2) k_hi = k_hi < m0 + SK_T ? k_hi : m0 + SK_T;
+  if (g.triB == 1) k_hi = k_hi < n0 + SK_T ? k_hi : n0 + SK_T;
+  if (g.triB == 2) k_lo = k_lo > n0 ? k_lo : n0;
+  k_lo = k_lo / SK_C * SK_C;
+  const int nch = k_hi > k_lo ? (int)((k_hi - k_lo + SK_C - 1) / SK_C) : 0;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const bool acc_c = g.beta != 0.0f;
+  const float a_scale = acc_c ? g.alpha : 1.0f;
+  const int64_t m = m0 + l32, n = n0 + l32;                    // this lane's row of A, column of B
+  const int64_t mc = m < g.M ? m : g.M - 1, nc = n < g.N ? n : g.N - 1;
+
+  // 16-byte loads need K % 4 == 0: then a clamped run only ever holds k >= K (zeroed)
+  const bool vec = g.vec && (g.K & 3) == 0;
+  floatx16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  for (int c = wave; c < nch; c += 4) {
+    const int64_t kb = k_lo + (int64_t)c * SK_C + 16 * h;     // first k of this lane
+    float a[16], b[16];
+    if (vec) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t k4 = kb + 4 * j < g.K - 4 ? kb + 4 * j : g.K - 4;
+        const floatx4 v = *reinterpret_cast<const floatx4*>(g.A + mc * g.lda + k4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[4 * j + e] = v[e];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t k = kb + i < g.K ? kb + i : g.K - 1;
+        a[i] = g.A[mc * g.lda + k];
+      }
+    }
+    if (TB && vec) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t k4 = kb + 4 * j < g.K - 4 ? kb + 4 * j : g.K - 4;
+        const floatx4 v = *reinterpret_cast<const floatx4*>(g.B + nc * g.ldb + k4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b[4 * j + e] = v[e];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t k = kb + i < g.K ? kb + i : g.K - 1;
+        b[i] = TB ? g.B[nc * g.ldb + k] : g.B[k * g.ldb + nc];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t k = kb + i;
+      a[i] = a_ok(g, m, k) ? a[i] * a_scale : 0.0f;
+      b[i] = b_ok(g, k, n) ? b[i] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], acc, 0, 0, 0);
+  }
+
+  // partial tiles -> LDS (row stride 33), summed in wave order by all 256 threads
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    red[wave * SK_T * 33 + (8 * (r >> 2) + 4 * h + (r & 3)) * 33 + l32] = acc[r];
+  __syncthreads();
+  const float out_scale = acc_c ? 1.0f : g.alpha;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid + 256 * q, mr = e / SK_T, ncl = e % SK_T;
+    const int o = mr * 33 + ncl;
+    float v = red[o];
+    v += red[SK_T * 33 + o];
+    v += red[2 * SK_T * 33 + o];
+    v += red[3 * SK_T * 33 + o];
+    const int64_t gm = m0 + mr, gn = n0 + ncl;
+    if (gm < g.M && gn < g.N && (g.triC == 0 || gm <= gn)) {
+      float* cp = g.C + gm * g.ldc + gn;
+      *cp = acc_c ? *cp + v : out_scale * v;
+    }
+  }
+}
+
+template <bool TB>
+__global__ void __launch_bounds__(256) gemm_f32_small(Dev g) {
+  __shared__ float red[4 * SK_T * 33];
+  small_tile<TB>(g, blockIdx.x, red);
+}
+
+template <bool TB1, bool TB2>
+__global__ void __launch_bounds__(256) gemm_f32_small_pair(Dev g1, int64_t tiles1, Dev g2) {
+  __shared__ float red[4 * SK_T * 33];
+  if ((int64_t)blockIdx.x < tiles1) small_tile<TB1>(g1, blockIdx.x, red);
+  else small_tile<TB2>(g2, (int64_t)blockIdx.x - tiles1, red);
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 template <int BM, int BN>
@@ -523,11 +658,28 @@ hipError_t launch(const Dev& g, bool ta, bool tb, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int NS>
 hipError_t launch_dma(const Dev& g, bool tb, hipStream_t s) {
   const int64_t grid = ceil_div(g.M, BM) * ceil_div(g.N, BN);
-  if (tb) hipLaunchKernelGGL((gemm_f32_dma<BM, BN, true>), dim3(grid), dim3(256), 0, s, g);
-  else hipLaunchKernelGGL((gemm_f32_dma<BM, BN, false>), dim3(grid), dim3(256), 0, s, g);
+  if (tb) hipLaunchKernelGGL((gemm_f32_dma<BM, BN, true, NS>), dim3(grid), dim3(256), 0, s, g);
+  else hipLaunchKernelGGL((gemm_f32_dma<BM, BN, false, NS>), dim3(grid), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_small(const Dev& g, bool tb, hipStream_t s) {
+  const int64_t grid = ceil_div(g.M, SK_T) * ceil_div(g.N, SK_T);
+  if (tb) hipLaunchKernelGGL((gemm_f32_small<true>), dim3(grid), dim3(256), 0, s, g);
+  else hipLaunchKernelGGL((gemm_f32_small<false>), dim3(grid), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_small_pair(const Dev& g1, bool tb1, const Dev& g2, bool tb2, hipStream_t s) {
+  const int64_t t1 = ceil_div(g1.M, SK_T) * ceil_div(g1.N, SK_T);
+  const int64_t grid = t1 + ceil_div(g2.M, SK_T) * ceil_div(g2.N, SK_T);
+  if (!tb1 && !tb2) hipLaunchKernelGGL((gemm_f32_small_pair<false, false>), dim3(grid), dim3(256), 0, s, g1, t1, g2);
+  else if (!tb1 && tb2) hipLaunchKernelGGL((gemm_f32_small_pair<false, true>), dim3(grid), dim3(256), 0, s, g1, t1, g2);
+  else if (tb1 && !tb2) hipLaunchKernelGGL((gemm_f32_small_pair<true, false>), dim3(grid), dim3(256), 0, s, g1, t1, g2);
+  else hipLaunchKernelGGL((gemm_f32_small_pair<true, true>), dim3(grid), dim3(256), 0, s, g1, t1, g2);
   return hipGetLastError();
 }
 
@@ -573,6 +725,11 @@ hipError_t gemm_f32_pair(const GemmArgs& a1, const GemmArgs& a2, hipStream_t str
   if (a1.transA || a2.transA || !valid_args(a1) || !valid_args(a2)) return hipErrorInvalidValue;
   const Dev g1 = make_dev(a1), g2 = make_dev(a2);
   ProfScope ps(prof_name, stream);
+  // few 64 x 64 tiles (at most one per CU): the short-K kernel puts four waves on each 32 x 32
+  // tile instead (measured on MI355X: 128^3 pair 9.9 -> 5.6 us, 512^3 22 -> 15 us; at 1024^3,
+  // 512 tiles, the 64 x 64 kernel is faster)
+  if (ceil_div(a1.M, 64) * ceil_div(a1.N, 64) + ceil_div(a2.M, 64) * ceil_div(a2.N, 64) <= 256)
+    return launch_small_pair(g1, a1.transB, g2, a2.transB, stream);
   const int64_t big = ceil_div(a1.M, 128) * ceil_div(a1.N, 128) + ceil_div(a2.M, 128) * ceil_div(a2.N, 128);
   const bool masked = (a1.triA || a1.triB || a1.triC || a2.triA || a2.triB || a2.triC) &&
                       big < 1024;
@@ -593,6 +750,10 @@ hipError_t gemm_f32(const GemmArgs& a, hipStream_t stream, const char* prof_name
   const Dev g = make_dev(a);
   const int vec = g.vec;
   ProfScope ps(prof_name, stream);
+  // At most one 64 x 64 tile per CU: the short-K kernel (measured on MI355X: 128^3 9.3 -> 4.9
+  // us, 1024^3 with a triangular operand 40 -> 28 us, 4096 x 128 x 128 11 -> 7.7 us)
+  if (!a.transA && ceil_div(a.M, 64) * ceil_div(a.N, 64) <= 256)
+    return launch_small(g, a.transB, stream);
   const int64_t big_tiles = ceil_div(a.M, 128) * ceil_div(a.N, 128);
   // With a triangular mask K differs per tile: while there are few 128 x 128 tiles per CU
   // (one would wait for the longest), 64 x 64 tiles, longest first, let the dispatcher
@@ -607,7 +768,7 @@ hipError_t gemm_f32(const GemmArgs& a, hipStream_t stream, const char* prof_name
   // (4096 x 2048 x 2048: 97 vs 91 TFLOP/s); for shorter K or fewer tiles the register-staged
   // kernel is as fast or faster (e.g. 1024^3: 61 vs 48 TFLOP/s).
   if (!masked && dma && big_tiles >= 256 && a.K >= 2048)
-    return launch_dma<128, 128>(g, a.transB, stream);
+    return launch_dma<128, 128, DNS>(g, a.transB, stream);
   if (!masked && big_tiles >= 192) return launch<128, 128>(g, a.transA, a.transB, stream);
   return launch<64, 64>(g, a.transA, a.transB, stream);
 }
