@@ -3,7 +3,8 @@
 // -(w_q - quant(w_q)) / [H^-1]_qq * H^-1_{:,q}, which through G = Cholesky(H^-1)^T is
 //     e = (w_q - w^_q) / G_qq,   w_k -= e * G_qk  (k > q).
 // Blocks of B columns: updates inside the block are immediate (quant_block), the columns
-// right of the block get one batch update W[:, end:] -= E G[blk, end:] (fp32 MFMA GEMM).
+// right of the block get the batch update W[:, end:] -= E G[blk, end:] (fp32 MFMA GEMM);
+// the batch updates of all blocks are grouped recursively by halves (solve, below).
 //
 // Quantizer (section 量化基础 of the same page; round and clip of the linear form on
 // the m.youleyou.com introduction, section 四): code = clip(rne(w/s + z), 0, 2^b - 1),
