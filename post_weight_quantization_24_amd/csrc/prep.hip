@@ -204,6 +204,27 @@ __device__ int diag_factor(float* sp, float* bc, int lane, int k_valid) {
   return bad;
 }
 
+// Load order of the ten upper sub-blocks (row block, column block): the one factored first,
+// then the panels it feeds, then the rest.
+__host__ __device__ constexpr int unit_q(int e) {
+  return e == 0 ? 3 : e == 1 ? 2 : e == 2 ? 1 : e == 3 ? 0 : e == 4 ? 2 : e == 5 ? 1 : e == 6 ? 0
+       : e == 7 ? 1 : 0;
+}
+__host__ __device__ constexpr int unit_r(int e) { return e <= 3 ? 3 : e <= 6 ? 2 : e <= 8 ? 1 : 0; }
+
+// Unit E of this thread into its slot; entries beyond n are the identity.
+template <int E>
+__device__ __forceinline__ void put_unit(float* slot, const floatx4& v, int rho, int kap, int n) {
+  constexpr int q = unit_q(E), r = unit_r(E);
+  const int i = LB * q + rho;
+  float* d = slot + slot_of(q, r) * SLOT + rho * LS + 4 * kap;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int jj = LB * r + 4 * kap + c;
+    d[c] = (i < n && jj < n) ? v[c] : (i == jj ? 1.0f : 0.0f);
+  }
+}
+
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 leaf_factor_invert(float* __restrict__ A, int64_t ld, int64_t off, int n, int* flag) {
   __shared__ float slot[NSLOT * SLOT];
@@ -214,46 +235,31 @@ leaf_factor_invert(float* __restrict__ A, int64_t ld, int64_t off, int n, int* f
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   float* blk = A + off * ld + off;
 
-  // Load the upper triangle into the slots: thread units of 4 consecutive columns of one
-  // row, every load issued before the first use (addresses clamped into the block, then
-  // selected); the padding beyond n is the identity.  Diagonal slots receive their upper
-  // triangle only (diag_factor reads no other part).
+  // Load the ten upper sub-blocks: unit e of every thread is row tid / 8, columns 4 (tid % 8)
+  // .. +3 of sub-block (unit_q(e), unit_r(e)), all loads issued at once (addresses clamped into the
+  // block, then selected; the padding beyond n is the identity).  Sub-block (3, 3) comes
+  // first: it is written to LDS before the first barrier so that its factorization starts
+  // while the other nine are still in flight; they are written during that iteration.
   const bool vec = ((reinterpret_cast<uintptr_t>(blk) | (uintptr_t)(ld * 4)) & 15) == 0 &&
                    (n & 3) == 0;
-  {
-    constexpr int UN = NB * NB / 4 / 256;
-    floatx4 v[UN];
-    if (vec) {
+  const int rho = tid >> 3, kap = tid & 7;
+  floatx4 v[NSLOT];
 #pragma unroll
-      for (int e = 0; e < UN; ++e) {
-        const int u = tid + 256 * e, i = u / (NB / 4), j0 = 4 * (u % (NB / 4));
-        const int ic = i < n ? i : n - 1, jc = j0 < n ? j0 : n - 4;
-        v[e] = *reinterpret_cast<const floatx4*>(blk + (ic * (int)ld + jc));
-      }
+  for (int e = 0; e < NSLOT; ++e) {
+    const int i = LB * unit_q(e) + rho, j0 = LB * unit_r(e) + 4 * kap;
+    const int ic = i < n ? i : n - 1;
+    if (vec) {
+      const int jc = j0 < n ? j0 : n - 4;
+      v[e] = *reinterpret_cast<const floatx4*>(blk + (ic * (int)ld + jc));
     } else {
 #pragma unroll
-      for (int e = 0; e < UN; ++e) {
-        const int u = tid + 256 * e, i = u / (NB / 4), j0 = 4 * (u % (NB / 4));
-        const int ic = i < n ? i : n - 1;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int jc = j0 + c < n ? j0 + c : n - 1;
-          v[e][c] = blk[ic * (int)ld + jc];
-        }
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < UN; ++e) {
-      const int u = tid + 256 * e, i = u / (NB / 4), j0 = 4 * (u % (NB / 4));
-      if (j0 / LB < i / LB) continue;   // below the diagonal sub-blocks
-      float* d = slot + slot_of(i / LB, j0 / LB) * SLOT + (i % LB) * LS + j0 % LB;
-#pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int jj = j0 + c;
-        d[c] = (i < n && jj < n) ? v[e][c] : (i == jj ? 1.0f : 0.0f);
+        const int jc = j0 + c < n ? j0 + c : n - 1;
+        v[e][c] = blk[ic * (int)ld + jc];
       }
     }
   }
+  put_unit<0>(slot, v[0], rho, kap, n);
   if (tid == 0) bad_at = INT_MAX;
   __syncthreads();
 
@@ -288,6 +294,17 @@ leaf_factor_invert(float* __restrict__ A, int64_t ld, int64_t off, int n, int* f
                                                 lane);
       }
     }
+    if (p == NLB - 1) {   // the other nine sub-blocks (wave 0 after its factorization)
+      put_unit<1>(slot, v[1], rho, kap, n);
+      put_unit<2>(slot, v[2], rho, kap, n);
+      put_unit<3>(slot, v[3], rho, kap, n);
+      put_unit<4>(slot, v[4], rho, kap, n);
+      put_unit<5>(slot, v[5], rho, kap, n);
+      put_unit<6>(slot, v[6], rho, kap, n);
+      put_unit<7>(slot, v[7], rho, kap, n);
+      put_unit<8>(slot, v[8], rho, kap, n);
+      put_unit<9>(slot, v[9], rho, kap, n);
+    }
     __syncthreads();
     int task = 0;
     for (int r = p + 1; r < NLB; ++r, ++task)            // G_pr = -G_pp T_pr
@@ -300,38 +317,27 @@ leaf_factor_invert(float* __restrict__ A, int64_t ld, int64_t off, int n, int* f
         block_prod<false, true, false, false>(ubuf + q * SLOT, slot + slot_of(q, p) * SLOT, gpp,
                                               lane);
     __syncthreads();
-  }
-
-  if (tid == 0 && bad_at != INT_MAX) atomicMin(flag, (int)(off + bad_at) + 1);
-  // Store whole rows of the block: the upper sub-blocks from the slots (diagonal ones hold
-  // zeros below the diagonal), zeros for the sub-blocks below them.  Entries below the
-  // diagonal of the matrix are don't-care until the final clearing pass.
-  {
-    constexpr int UN = NB * NB / 4 / 256;
-    floatx4 g[UN];
+    // Row block p of G is final (later iterations only read it): store its sub-blocks
+    // (p, r >= p) while the next iterations run.  The sub-blocks left of the diagonal ones
+    // are strictly lower entries, which every later product masks and the final pass clears.
 #pragma unroll
-    for (int e = 0; e < UN; ++e) {
-      const int u = tid + 256 * e, i = u / (NB / 4), j0 = 4 * (u % (NB / 4));
-      const int bi = i / LB, bj = j0 / LB < bi ? bi : j0 / LB;
-      const float* src = slot + slot_of(bi, bj) * SLOT + (i % LB) * LS + j0 % LB;
-      const bool up = j0 / LB >= bi;
-      g[e] = floatx4{up ? src[0] : 0.0f, up ? src[1] : 0.0f, up ? src[2] : 0.0f,
-                     up ? src[3] : 0.0f};
-    }
-    const int ld32 = (int)ld;
-#pragma unroll
-    for (int e = 0; e < UN; ++e) {
-      const int u = tid + 256 * e, i = u / (NB / 4), j0 = 4 * (u % (NB / 4));
-      float* dst = blk + (i * ld32 + j0);
+    for (int r = 0; r < NLB; ++r) {
+      if (r < p) continue;
+      const int i = LB * p + rho, j0 = LB * r + 4 * kap;
+      const float* s = slot + slot_of(p, r) * SLOT + rho * LS + 4 * kap;
+      const floatx4 g = floatx4{s[0], s[1], s[2], s[3]};
+      float* dst = blk + (i * (int)ld + j0);
       if (vec) {
-        if (i < n && j0 < n) *reinterpret_cast<floatx4*>(dst) = g[e];
+        if (i < n && j0 < n) *reinterpret_cast<floatx4*>(dst) = g;
       } else {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          if (i < n && j0 + c < n) dst[c] = g[e][c];
+          if (i < n && j0 + c < n) dst[c] = g[c];
       }
     }
   }
+
+  if (tid == 0 && bad_at != INT_MAX) atomicMin(flag, (int)(off + bad_at) + 1);
 }
 
 // Split of an n-block: the leading m columns (a multiple of the leaf size) and the rest.
