@@ -32,7 +32,7 @@ __device__ __forceinline__ void tile_coords(int tile, int& ti, int& tj) {
 // ---------------------------------------------------------------------------------
 // f16 inputs, direct-to-LDS pipeline (the launch path).
 //
-// Each stage holds 32 tokens x 256 channels of the two channel blocks, copied from X by
+// Each stage holds 64 tokens x 256 channels of the two channel blocks, copied from X by
 // buffer loads that write LDS directly (the buffer covers exactly the workgroup's token
 // range, so reads past its end return zeros: no masking for ragged token counts).  LDS
 // keeps X's token-major layout; the MFMA operands (8 consecutive tokens of one channel per
@@ -41,10 +41,15 @@ __device__ __forceinline__ void tile_coords(int tile, int& ti, int& tj) {
 // so lane j pointing at (token k0 + j/4, channels c0 + 4(j%4)..) hands lane i channel c0+i
 // at tokens k0..k0+3.  The 16-byte slots of a token row are XOR-swizzled by 4*(row % 4)
 // so that the four rows such a group touches fall on distinct banks.
-// Loads run three stages ahead of the MFMAs; each stage is a separate LDS array so that
-// waiting for one stage never waits for the loads of the later ones.
-constexpr int V2_BK = 32;                                 // tokens per stage
-constexpr int V2_STAGE_HALFS = V2_BK * TILE;              // 8192 halfs = 16 KB per operand
+// Two stages: the copies of stage s + 1 are issued, between the MFMAs, while stage s is
+// multiplied.  Measured on MI355X (q_proj, 11 splits, identical H): 64-token stages in a ring
+// of 2 run 2-4 % faster than 32-token stages in a ring of 4 (same 128 KB of LDS, half the
+// barriers); rings of 3 or 6 stages were 15 % slower.
+constexpr int V2_BK = 64;                                 // tokens per stage
+constexpr int V2_NST = 2;                                 // stages in the ring
+constexpr int V2_CPO = V2_BK / 2 / 4;                     // 1 KB copies per operand, wave, stage
+constexpr int V2_STAGE_HALFS = V2_BK * TILE;              // 16384 halfs = 32 KB per operand
+static_assert(V2_BK % 16 == 0 && V2_BK / 4 == 2 * V2_CPO, "one copy slot per MFMA group");
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) short4v lds_s4;
@@ -102,8 +107,8 @@ __device__ __forceinline__ void dma16(rsrc_t rsrc, uint32_t lds_base, int voff) 
                    : "memory", "m0");
 }
 
-// Copy q (0..15) of one operand's stage: a wave-wide 1 KB copy of token rows 2q, 2q+1
-// (16 copies per operand and stage, 4 per wave).
+// Copy q (0..V2_BK/2 - 1) of one operand's stage: a wave-wide 1 KB copy of token rows 2q,
+// 2q+1 (V2_CPO per wave).
 __device__ __forceinline__ void v2_load_copy(rsrc_t rsrc, short* dst, int tok_in_range, int64_t ldx,
                                              int64_t ch0, int q, int lane) {
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)dst);
@@ -136,6 +141,16 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// vmcnt wait that leaves `later` stages of CPW copies each in flight (later <= I)
+template <int CPW, int I>
+__device__ __forceinline__ void wait_later(int later) {
+  if constexpr (I <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (later >= I) wait_vmcnt<I * CPW>();
+    else wait_later<CPW, I - 1>(later);
+  }
+}
 // Workgroup barrier without the memory fence of __syncthreads (whose release half would
 // drain every outstanding load, including the stages meant to stay in flight).  The caller
 // has waited for the loads it needs; lgkmcnt(0) retires this wave's LDS reads first.
@@ -148,8 +163,8 @@ __global__ void __launch_bounds__(256, 1)
 hess_f16_lds(const _Float16* __restrict__ X, int64_t ldx, int64_t d, int64_t n_tok,
              int64_t tok_per_split, int tiles, int padded_tiles, int splits,
              float* __restrict__ part) {
-  // 4 stages x {A, B} x 32 tokens x 256 channels
-  __shared__ __attribute__((aligned(16))) short lds[4 * 2 * V2_STAGE_HALFS];
+  // V2_NST stages x {A, B} x V2_BK tokens x 256 channels
+  __shared__ __attribute__((aligned(16))) short lds[V2_NST * 2 * V2_STAGE_HALFS];
 
   int split, ti, tj;
   hess_work(blockIdx.x, padded_tiles, splits, split, ti, tj);
@@ -183,37 +198,35 @@ hess_f16_lds(const _Float16* __restrict__ X, int64_t ldx, int64_t d, int64_t n_t
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-  auto stage_a = [&](int st) { return lds + (st & 3) * 2 * V2_STAGE_HALFS; };
-  // copy i (0..7) of this wave's share of stage st: 0..3 operand A, 4..7 operand B
+  auto stage_a = [&](int st) { return lds + (st % V2_NST) * 2 * V2_STAGE_HALFS; };
+  // copy i (0 .. 2 V2_CPO - 1) of this wave's share of stage st: operand A, then operand B
   auto issue_part = [&](int st, int i) {
-    short* dst = stage_a(st) + (i >= 4 ? V2_STAGE_HALFS : 0);
-    v2_load_copy(rsrc, dst, st * V2_BK, ldx, i >= 4 ? cb0 : ca0, wave * 4 + (i & 3), lane);
+    short* dst = stage_a(st) + (i >= V2_CPO ? V2_STAGE_HALFS : 0);
+    v2_load_copy(rsrc, dst, st * V2_BK, ldx, i >= V2_CPO ? cb0 : ca0,
+                 wave * V2_CPO + (i % V2_CPO), lane);
   };
   auto issue = [&](int st) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) issue_part(st, i);
+    for (int i = 0; i < V2_CPO; ++i) issue_part(st, i);
     if (!diag) {
 #pragma unroll
-      for (int i = 4; i < 8; ++i) issue_part(st, i);
+      for (int i = V2_CPO; i < 2 * V2_CPO; ++i) issue_part(st, i);
     }
   };
 
-  if (nsteps > 0) issue(0);
-  if (nsteps > 1) issue(1);
-  if (nsteps > 2) issue(2);
+#pragma unroll
+  for (int i = 0; i < V2_NST - 1; ++i)
+    if (i < nsteps) issue(i);
   for (int s = 0; s < nsteps; ++s) {
     // stage s has landed once at most `later` stages issued after it are pending
-    // (copies retire in order; 4 per operand per wave and stage)
-    const int later = nsteps - 1 - s < 2 ? nsteps - 1 - s : 2;
-    if (diag) {
-      if (later == 2) wait_vmcnt<8>(); else if (later == 1) wait_vmcnt<4>(); else wait_vmcnt<0>();
-    } else {
-      if (later == 2) wait_vmcnt<16>(); else if (later == 1) wait_vmcnt<8>(); else wait_vmcnt<0>();
-    }
+    // (copies retire in order; V2_CPO per operand per wave and stage)
+    const int later = nsteps - 1 - s < V2_NST - 2 ? nsteps - 1 - s : V2_NST - 2;
+    if (diag) wait_later<V2_CPO, V2_NST - 2>(later);
+    else wait_later<2 * V2_CPO, V2_NST - 2>(later);
     stage_barrier();
-    // stage s + 3 goes into the buffer read in iteration s - 1; its copies are spread
-    // between the MFMAs so that a stalled copy issue does not leave the matrix core idle
-    const bool more = s + 3 < nsteps;
+    // stage s + V2_NST - 1 goes into the buffer read in iteration s - 1; its copies are
+    // spread between the MFMAs so that a stalled copy issue does not leave the matrix core idle
+    const bool more = s + V2_NST - 1 < nsteps;
     const short* sa = stage_a(s);
     const short* sb = diag ? sa : sa + V2_STAGE_HALFS;
 #pragma unroll
@@ -228,8 +241,8 @@ hess_f16_lds(const _Float16* __restrict__ X, int64_t ldx, int64_t d, int64_t n_t
 #pragma unroll
         for (int b = 0; b < 4; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
-        const int part = kk * 4 + a;
-        if (more && (part < 4 || !diag)) issue_part(s + 3, part);
+        const int part = kk * 4 + a;   // V2_BK / 4 = 2 V2_CPO slots per stage
+        if (more && (part < V2_CPO || !diag)) issue_part(s + V2_NST - 1, part);
       }
     }
   }
