@@ -733,7 +733,7 @@ hipError_t gemm_f32_pair(const GemmArgs& a1, const GemmArgs& a2, hipStream_t str
   const int64_t big = ceil_div(a1.M, 128) * ceil_div(a1.N, 128) + ceil_div(a2.M, 128) * ceil_div(a2.N, 128);
   const bool masked = (a1.triA || a1.triB || a1.triC || a2.triA || a2.triB || a2.triC) &&
                       big < 1024;
-  if (!masked && big >= 192) return launch_pair<128, 128>(g1, a1.transB, g2, a2.transB, stream);
+  if (!masked && big >= 512) return launch_pair<128, 128>(g1, a1.transB, g2, a2.transB, stream);
   return launch_pair<64, 64>(g1, a1.transB, g2, a2.transB, stream);
 }
 
@@ -764,12 +764,12 @@ hipError_t gemm_f32(const GemmArgs& a, hipStream_t stream, const char* prof_name
   const bool dma = vec && !a.transA && a.K % 4 == 0 && a.K >= 4 && (a.transB || a.N % 4 == 0) &&
                    a.M >= 64 && a.N >= 64 && a.lda < ((int64_t)1 << 21) &&
                    a.ldb < ((int64_t)1 << 21);
-  // Measured on MI355X: the direct-to-LDS kernel only wins for long K on large outputs
-  // (4096 x 2048 x 2048: 97 vs 91 TFLOP/s); for shorter K or fewer tiles the register-staged
-  // kernel is as fast or faster (e.g. 1024^3: 61 vs 48 TFLOP/s).
-  if (!masked && dma && big_tiles >= 256 && a.K >= 2048)
+  // Measured on MI355X: 128 x 128 tiles pay off from about two per CU (4096 x 1024 x 1024:
+  // 64 x 64 tiles 98 us, 128 x 128 120 us; 4096 x 2048 x 2048: all variants 330-345 us); the
+  // direct-to-LDS kernel only for long K on large outputs.
+  if (!masked && dma && big_tiles >= 512 && a.K >= 2048)
     return launch_dma<128, 128, DNS>(g, a.transB, stream);
-  if (!masked && big_tiles >= 192) return launch<128, 128>(g, a.transA, a.transB, stream);
+  if (!masked && big_tiles >= 512) return launch<128, 128>(g, a.transA, a.transB, stream);
   return launch<64, 64>(g, a.transA, a.transB, stream);
 }
 
