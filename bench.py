@@ -87,6 +87,8 @@ def family_work(fam, d_row, d_col, n_tok, bits, block, x_dtype):
         return d_row * d_col * (8 + bits / 8) + d_col * block * 4, "GB/s", hbm, "hbm"
     if fam == "quant_convert":
         return d_row * d_col * 6, "GB/s", hbm, "hbm"
+    if fam == "quant_group_params":  # each group's columns read once, scales and zeros written
+        return d_row * d_col * 4, "GB/s", hbm, "hbm"
     if fam == "hessian_reduce":    # H read and written (the partial tiles are extra)
         return d_col * d_col * 8, "GB/s", hbm, "hbm"
     return d_col * d_col * 8, "GB/s", hbm, "hbm"
@@ -250,6 +252,14 @@ def main():
     G.profile_enable(False)
     phases = read_phases(1)
     dom = max(phases, key=lambda k: phases[k]["ms_per_step"])
+    for f, ph in phases.items():     # each family against its own roofline (this one step)
+        work, unit, peak, bound = family_work(f, d_row, d_col, n_tok, bits, block, wl.dtype)
+        ach = work / (ph["ms_per_step"] / 1e3) / (1e12 if unit == "TFLOP/s" else 1e9)
+        ph.update({"bound": bound, "achieved": ach, "peak": peak, "unit": unit,
+                   "frac": ach / peak})
+    quant_ms = sum(phases[f]["ms_per_step"] for f in
+                   ("quant_convert", "quant_group_params", "quant_block", "lazy_gemm")
+                   if f in phases)
 
     # ---- timed region: K steps; HIP events around the dominant kernel's launches only
     G.profile_reset()
@@ -299,6 +309,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "phases": phases,
+        # the column solve alone (G given), from the same profiled step as the phase table
+        "quantize_only": {"value": d_row * d_col / (quant_ms / 1e3), "unit": "weights/s"},
         "input_gen_s": gen_s,
     }
     print(json.dumps(out))
