@@ -37,7 +37,9 @@ brute-force Hessian, G^T G H_d = I and agreement of two independent G routes,
 the literal OBS formula with explicit inverses, the conditional least-squares
 re-fit, H proportional to I giving round-to-nearest exactly, the identity
 sum(e^2) = Delta H_d Delta^T, Delta = E G, blocked = unblocked, invariance to X
-scaling, GPTQ <= RTN, grid membership, exact ties, pack/unpack and known words.
+scaling, GPTQ <= RTN, grid membership, exact ties, pack/unpack and known words;
+dequant_matvec: hand-computed products over known words (INT4, INT3 straddling words,
+INT2), the hand-solved 1x2 layer, and sum_t ||W x_t - y_t||^2 = 1/2 sum_r D_r H D_r^T.
 No function here is "parity unpinned".
 """
 
@@ -51,7 +53,7 @@ __all__ = [
     "hessian", "damp", "inv_chol_upper", "inv_chol_upper_reversed", "prepare_g",
     "group_params", "quantize_values", "gptq_quantize", "gptq_quantize_obs_literal",
     "rtn_quantize", "dequantize", "layer_loss", "direct_loss", "pack_codes", "unpack_codes",
-    "quant_range", "TIE_TOL",
+    "quant_range", "TIE_TOL", "dequant_matvec",
 ]
 
 TIE_TOL = 1e-3   # a v within this many steps of k + 1/2 is a near-tie (either code accepted)
@@ -330,6 +332,25 @@ def direct_loss(W, w_hat, X) -> float:
     D = np.asarray(W, dtype=np.float64) - np.asarray(w_hat, dtype=np.float64)
     Y = np.asarray(X, dtype=np.float64) @ D.T
     return float(np.sum(Y * Y))
+
+
+# --------------------------------------------------------------------------- next: W4A16
+
+def dequant_matvec(words: np.ndarray, scales: np.ndarray, zeros: np.ndarray, bits: int,
+                   group: int, d_col: int, x) -> np.ndarray:
+    """Weight-only quantized linear layer, y = x W^T with W^ read from the packed format:
+    y[n, r] = sum_c x[n, c] * s[r, c // g] * (code[r, c] - z[r, c // g]), in float64.
+
+    Page "量化": section GPTQ (the quantized layer computes W X; its output is per-channel
+    INT4 for memory-bound single-batch inference) and section AWQ (W4A16: INT4 weights with
+    FP16 activations; the dequantization belongs to the matrix product itself, no FP16
+    weight matrix is written).  Here the product is taken literally from its definition:
+    unpack, dequantize, multiply.  x is [n, d_col] (fp16 values widened), y is [n, d_row].
+    """
+    g = d_col if group == 0 else group
+    codes = unpack_codes(words, bits, d_col)
+    w_hat = dequantize(codes, scales, zeros, g)
+    return np.asarray(x, dtype=np.float64) @ w_hat.T
 
 
 # --------------------------------------------------------------------------- a7
