@@ -153,10 +153,33 @@ int gptq_dequant_check(const uint32_t* qweight, const float* scales, const uint8
                        const gptq_spec* spec, double* loss, double* row_loss, float* W_hat,
                        int64_t* off_grid, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- weight-only product
+ * Quantized linear layer over the packed output of gptq_quantize_layer, for a few fp16
+ * activation rows (W4A16 and its 2/3/8-bit kin: page "量化", section AWQ, weights in 4 bits
+ * and activations in fp16 with the dequantization inside the matrix product; section GPTQ,
+ * per-channel INT4 weights for memory-bound single-batch inference):
+ *     y[i][r] = sum_c x[i][c] * scales[r][c / g] * (code(r, c) - zeros[r][c / g])
+ * with code(r, c) at bits [c*bits, c*bits + bits) of row r's little-endian bitstream in
+ * qweight, exactly as gptq_quantize_layer writes it (g = d_col when group = 0).
+ *   qweight  [d_row x d_col*bits/32] uint32, 16-byte aligned; scales [d_row x d_col/g]
+ *            fp32; zeros [d_row x d_col/g] uint8.
+ *   x        [n x d_col] fp16 (x_dtype must be GPTQ_F16), row stride ldx >= d_col.
+ *   y        [n x d_row] fp32 output, row stride ldy >= d_row.
+ *   bits 2, 3, 4 or 8; group 0 (per-channel) or a multiple of 32 dividing d_col;
+ *   d_col a multiple of 32 and at most 32768; 1 <= n <= 4096 (the rows are taken in groups
+ *   whose fp16 copy fits 64 KB of LDS, at most 8 per launch).
+ * Products are accumulated in fp32 (fp16 products of the exact integers q - z for 4 bits),
+ * one run of 32 codes at a time, then over runs in a fixed order: deterministic.
+ * Errors: GPTQ_EINVAL for NULL pointers, shapes, strides or alignment; GPTQ_EHIP. */
+int gptq_dequant_matvec(const uint32_t* qweight, const float* scales, const uint8_t* zeros,
+                        int64_t d_row, int64_t d_col, int bits, int group, const void* x,
+                        int x_dtype, int64_t n, int64_t ldx, float* y, int64_t ldy,
+                        void* stream);
+
 /* ---------------------------------------------------------------- instrumentation
  * Optional per-kernel timing with HIP events recorded on the caller's stream around
  * every launch of the named kernel family ("hessian_mfma", "hessian_reduce", "prep_leaf",
- * "prep_gemm", "quant_block", "lazy_gemm", ...).  Enabling costs two event records per
+ * "prep_gemm", "quant_block", "lazy_gemm", "dequant_matvec", ...).  Enabling costs two event records per
  * timed launch; gptq_profile_only(name) restricts timing to one family (NULL: all).
  * gptq_profile_read returns the number of timed launches and their summed duration in
  * milliseconds (waits for the recorded events).  For measurement, not for production. */

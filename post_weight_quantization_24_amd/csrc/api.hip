@@ -270,6 +270,31 @@ int gptq_dequant_check(const uint32_t* qweight, const float* scales, const uint8
   return GPTQ_OK;
 }
 
+int gptq_dequant_matvec(const uint32_t* qweight, const float* scales, const uint8_t* zeros,
+                        int64_t d_row, int64_t d_col, int bits, int group, const void* x,
+                        int x_dtype, int64_t n, int64_t ldx, float* y, int64_t ldy,
+                        void* stream) {
+  g_last_error.clear();
+  int rc;
+  if ((rc = check_layer(GPTQ_F16, d_row, d_col)) != GPTQ_OK) return rc;
+  if (d_col > 32768) return fail(GPTQ_EINVAL, "d_col must be at most 32768 (got %lld)", (long long)d_col);
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
+    return fail(GPTQ_EINVAL, "bits must be 2, 3, 4 or 8 (got %d)", bits);
+  if (group < 0 || (group > 0 && (group % 32 != 0 || d_col % group != 0)))
+    return fail(GPTQ_EINVAL, "group must be 0 or a multiple of 32 dividing d_col (got %d)", group);
+  if (x_dtype != GPTQ_F16) return fail(GPTQ_EINVAL, "x must be fp16 (GPTQ_F16)");
+  if (n < 1 || n > 4096) return fail(GPTQ_EINVAL, "n must be in [1, 4096] (got %lld)", (long long)n);
+  if (ldx < d_col || ldy < d_row) return fail(GPTQ_EINVAL, "ldx >= d_col and ldy >= d_row required");
+  if (!qweight || !scales || !zeros || !x || !y)
+    return fail(GPTQ_EINVAL, "qweight, scales, zeros, x and y must not be NULL");
+  if (!aligned(qweight, 16) || !aligned(x, 4))
+    return fail(GPTQ_EINVAL, "qweight must be 16-byte aligned and x 4-byte aligned");
+  hipError_t e = gptq::matvec_launch(qweight, scales, zeros, d_row, d_col, bits, group, x, n, ldx,
+                                     y, ldy, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gptq_dequant_matvec");
+  return GPTQ_OK;
+}
+
 // ---------------------------------------------------------------- instrumentation
 int gptq_profile_enable(int on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);

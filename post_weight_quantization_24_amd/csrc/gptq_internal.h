@@ -78,6 +78,13 @@ hipError_t check_launch(const uint32_t* qweight, const float* scales, const uint
                         int bits, int group, double* loss, double* row_loss, float* W_hat,
                         int64_t* off_grid, void* ws, hipStream_t stream);
 
+// ---------------------------------------------------------------- weight-only product (gemv.hip)
+// y[n x d_row] = x[n x d_col] (fp16) * W^T with W^ = s (code - z) read from the packed format.
+int64_t matvec_max_rows_per_launch(int64_t d_col);
+hipError_t matvec_launch(const uint32_t* qweight, const float* scales, const uint8_t* zeros,
+                         int64_t d_row, int64_t d_col, int bits, int group, const void* x,
+                         int64_t n, int64_t ldx, float* y, int64_t ldy, hipStream_t stream);
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
 

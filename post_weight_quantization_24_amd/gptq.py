@@ -51,6 +51,8 @@ _SIGS = {
     "gptq_check_workspace_size": ([_i64, _i64], _sz),
     "gptq_dequant_check": ([_vp, _vp, _vp, _vp, _int, _vp, _i64, _i64, ctypes.POINTER(Spec), _vp,
                             _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "gptq_dequant_matvec": ([_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _int, _i64, _i64, _vp,
+                             _i64, _vp], _int),
     "gptq_profile_enable": ([_int], _int),
     "gptq_profile_only": ([ctypes.c_char_p], _int),
     "gptq_profile_reset": ([], _int),
@@ -197,6 +199,22 @@ def dequant_check(qweight, scales, zeros, W, H, spec: Spec, want_w_hat=False, ws
                                     off.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
                                     _stream_handle(stream)))
     return loss, row_loss, w_hat, off
+
+
+def dequant_matvec(qweight, scales, zeros, x, bits: int, group: int, d_col: int, y=None,
+                   stream=None):
+    """y [n x d_row] fp32 = x [n x d_col] fp16 times the dequantized packed weights, transposed
+    (gptq_dequant_matvec)."""
+    torch = _torch()
+    d_row = qweight.shape[0]
+    n = x.shape[0]
+    if y is None:
+        y = torch.empty((n, d_row), dtype=torch.float32, device=x.device)
+    _check(lib().gptq_dequant_matvec(qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                                     d_row, d_col, bits, group, x.data_ptr(), _dtype_code(x), n,
+                                     x.stride(0), y.data_ptr(), y.stride(0),
+                                     _stream_handle(stream)))
+    return y
 
 
 def profile_enable(on=True):

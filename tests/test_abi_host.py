@@ -125,3 +125,22 @@ def test_profile_calls_without_gpu(lib):
     G.profile_enable(False)
     G.profile_reset()
     assert G.profile_read("hessian_mfma") == (0, 0.0)
+
+
+def test_matvec_validation(lib):
+    f = lib.gptq_dequant_matvec
+    # qweight, scales, zeros, d_row, d_col, bits, group, x, x_dtype, n, ldx, y, ldy, stream
+    ok = (FAKE, FAKE, FAKE, 64, 256, 4, 128, FAKE, G.F16, 1, 256, FAKE, 64)
+    assert f(*ok[:3], 64, 250, *ok[5:], None) == G.EINVAL               # d_col % 32
+    assert f(*ok[:3], 64, 32768 + 32, 4, 0, *ok[7:], None) == G.EINVAL  # d_col too large
+    assert b"32768" in lib.gptq_last_error()
+    assert f(*ok[:5], 5, *ok[6:], None) == G.EINVAL                     # bits
+    assert f(*ok[:6], 16, *ok[7:], None) == G.EINVAL                    # group % 32
+    assert f(*ok[:6], 96, *ok[7:], None) == G.EINVAL                    # group does not divide
+    assert f(*ok[:8], G.F32, *ok[9:], None) == G.EINVAL                 # fp16 activations only
+    assert f(*ok[:9], 0, *ok[10:], None) == G.EINVAL                    # n
+    assert f(*ok[:10], 128, *ok[11:], None) == G.EINVAL                 # ldx < d_col
+    assert f(*ok[:12], 32, None) == G.EINVAL                            # ldy < d_row
+    assert f(None, *ok[1:], None) == G.EINVAL
+    assert f(*ok[:11], None, 64, None) == G.EINVAL
+    assert f(ctypes.c_void_p(0x10004), *ok[1:], None) == G.EINVAL       # qweight alignment
