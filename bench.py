@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--bits", type=int, default=None)
     p.add_argument("--block", type=int, default=None)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-w4a16", action="store_true",
+                   help="skip the weight-only quantized product leg")
     p.add_argument("--cpu-tokens", type=int, default=16384)
     p.add_argument("--cpu-rows", type=int, default=128)
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -121,6 +123,37 @@ def kernel_traffic(path, family, **cfg):
             return None
         return e["hbm_bytes_per_launch"]
     return None
+
+
+def w4a16_leg(G, torch, dev, layers, reps=100):
+    """The weight-only quantized product over packed weights (one fp16 activation row): average
+    launch time from HIP events on the launch stream, against the HBM roofline.  Algorithmic
+    bytes per launch: the packed codes, the scales and zeros, x and y."""
+    out = []
+    for name, qw, sc, ze, bits, group in layers:
+        d_row, d_col = qw.shape[0], qw.shape[1] * 32 // bits
+        g = d_col if group == 0 else group
+        x = torch.randn((1, d_col), device=dev).to(torch.float16)
+        y = torch.empty((1, d_row), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            G.dequant_matvec(qw, sc, ze, x, bits, group, d_col, y=y)
+        torch.cuda.synchronize()
+        G.profile_reset()
+        G.profile_only("dequant_matvec")
+        G.profile_enable(True)
+        for _ in range(reps):
+            G.dequant_matvec(qw, sc, ze, x, bits, group, d_col, y=y)
+        torch.cuda.synchronize()
+        G.profile_enable(False)
+        G.profile_only(None)
+        n, ms = G.profile_read("dequant_matvec")
+        avg_s = ms / n / 1e3
+        nbytes = d_row * d_col * bits // 8 + d_row * (d_col // g) * 5 + d_col * 2 + d_row * 4
+        ach = nbytes / avg_s / 1e9
+        out.append({"layer": name, "d_row": d_row, "d_col": d_col, "bits": bits, "group": group,
+                    "n": 1, "avg_launch_us": avg_s * 1e6, "bytes_per_launch": nbytes,
+                    "achieved": ach, "peak": PEAK["hbm"], "unit": "GB/s", "frac": ach / PEAK["hbm"]})
+    return out
 
 
 def cpu_baseline(W, X_sample, n_tok_full, spec, rows):
@@ -285,6 +318,22 @@ def main():
                 "frac": achieved / peak, "traffic": traffic, "kernel": dom,
                 "work_per_launch": work / launches_per_step}
 
+    # ---- the weight-only quantized product over packed weights: this layer's GPTQ output and
+    # a 70B-shaped gate_proj (28672 x 8192 INT4 g128, random packed codes)
+    w4 = None
+    if not a.no_w4a16:
+        big_rows, big_cols = 28672, 8192
+        bq = torch.randint(-2 ** 31, 2 ** 31 - 1, (big_rows, big_cols * 4 // 32), dtype=torch.int32,
+                           device=dev)
+        bs = torch.rand((big_rows, big_cols // 128), device=dev) * 0.02 + 0.002
+        bz = torch.randint(0, 16, (big_rows, big_cols // 128), dtype=torch.uint8, device=dev)
+        layers = [("%s %dx%d (GPTQ output of this bench)" % (layer.name, d_row, d_col), qweight,
+                   scales, zeros, bits, wl.group),
+                  ("gate_proj 28672x8192 INT4 g128 (random codes)", bq, bs, bz, 4, 128)]
+        own_ok = wl.group % 32 == 0 and d_col <= 32768      # the call's shape limits
+        w4 = w4a16_leg(G, torch, dev, layers if own_ok else layers[1:])
+        del bq, bs, bz
+
     cpu = None
     if not a.no_cpu:
         cpu = cpu_baseline(W, X_sample, n_tok, spec_d, min(a.cpu_rows, d_row))
@@ -311,6 +360,7 @@ def main():
         "phases": phases,
         # the column solve alone (G given), from the same profiled step as the phase table
         "quantize_only": {"value": d_row * d_col / (quant_ms / 1e3), "unit": "weights/s"},
+        "w4a16": w4,
         "input_gen_s": gen_s,
     }
     print(json.dumps(out))
