@@ -333,6 +333,22 @@ def main():
         own_ok = wl.group % 32 == 0 and d_col <= 32768      # the call's shape limits
         w4 = w4a16_leg(G, torch, dev, layers if own_ok else layers[1:])
         del bq, bs, bz
+        # context: the same product with fp16 weights through the library GEMM (torch), the
+        # unquantized alternative whose 4x larger weight read the packed format avoids
+        w16 = torch.randn((big_rows, big_cols), device=dev).to(torch.float16)
+        xb = torch.randn((1, big_cols), device=dev).to(torch.float16)
+        for _ in range(3):
+            torch.matmul(xb, w16.t())
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(50):
+            torch.matmul(xb, w16.t())
+        e1.record()
+        torch.cuda.synchronize()
+        ref_us = e0.elapsed_time(e1) / 50 * 1e3
+        w4[-1]["fp16_library_us"] = ref_us
+        w4[-1]["speedup_vs_fp16"] = ref_us / w4[-1]["avg_launch_us"]
+        del w16, xb
 
     cpu = None
     if not a.no_cpu:
