@@ -41,15 +41,21 @@ __device__ __forceinline__ void tile_coords(int tile, int& ti, int& tj) {
 // so lane j pointing at (token k0 + j/4, channels c0 + 4(j%4)..) hands lane i channel c0+i
 // at tokens k0..k0+3.  The 16-byte slots of a token row are XOR-swizzled by 4*(row % 4)
 // so that the four rows such a group touches fall on distinct banks.
-// Two stages: the copies of stage s + 1 are issued, between the MFMAs, while stage s is
-// multiplied.  Measured on MI355X (q_proj, 11 splits, identical H): 64-token stages in a ring
-// of 2 run 2-4 % faster than 32-token stages in a ring of 4 (same 128 KB of LDS, half the
-// barriers); rings of 3 or 6 stages were 15 % slower.
+// Eight waves in a 2 x 4 grid, each owning a 128 x 64 quarter-column of the tile (128
+// accumulator registers), so two waves share each SIMD and one wave's MFMAs cover the
+// other's LDS waits.  Against four waves of 128 x 128 (one per SIMD) this reads 1.5x the
+// operand bytes from LDS but ran 6-8 % faster on MI355X (q_proj, 11 splits, identical H).
+// Two stages: the copies of stage s + 1 are issued, between the first MFMAs, while stage s
+// is multiplied.  Measured on MI355X: 64-token stages in a ring of 2 beat 32-token stages in
+// rings of 2, 3 or 4; issuing the copies all at once after the barrier, or spread over all
+// the MFMAs of a stage, was 4-6 % slower.
 constexpr int V2_BK = 64;                                 // tokens per stage
 constexpr int V2_NST = 2;                                 // stages in the ring
-constexpr int V2_CPO = V2_BK / 2 / 4;                     // 1 KB copies per operand, wave, stage
+constexpr int V2_WAVES = 8;                               // 2 x 4 wave grid
+constexpr int V2_BFR = 2;                                 // 32-column B fragments per wave
+constexpr int V2_CPO = V2_BK / 2 / V2_WAVES;              // 1 KB copies per operand, wave, stage
 constexpr int V2_STAGE_HALFS = V2_BK * TILE;              // 16384 halfs = 32 KB per operand
-static_assert(V2_BK % 16 == 0 && V2_BK / 4 == 2 * V2_CPO, "one copy slot per MFMA group");
+static_assert(V2_BK % 16 == 0 && V2_BK / 4 >= 2 * V2_CPO, "a copy slot per MFMA group");
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) short4v lds_s4;
@@ -159,7 +165,7 @@ __device__ __forceinline__ void stage_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(64 * V2_WAVES, 1)
 hess_f16_lds(const _Float16* __restrict__ X, int64_t ldx, int64_t d, int64_t n_tok,
              int64_t tok_per_split, int tiles, int padded_tiles, int splits,
              float* __restrict__ part) {
@@ -180,7 +186,7 @@ hess_f16_lds(const _Float16* __restrict__ X, int64_t ldx, int64_t d, int64_t n_t
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (LDS base in M0)
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;   // rows wm * 128 .., columns wn * 64 ..
   // buffer over exactly this workgroup's tokens; bytes beyond it read as zero
   // (built from readfirstlane'd values so that it lives in scalar registers)
   const uint64_t base = reinterpret_cast<uint64_t>(X + (n_here ? t_begin : 0) * ldx);
@@ -190,11 +196,11 @@ hess_f16_lds(const _Float16* __restrict__ X, int64_t ldx, int64_t d, int64_t n_t
   // buffer descriptor: base, stride 0, size in bytes, raw 32-bit data format
   const rsrc_t rsrc = {base_lo, base_hi & 0xffffu, (uint32_t)nbytes, 0x00020000u};
 
-  floatx16 acc[4][4];
+  floatx16 acc[4][V2_BFR];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < V2_BFR; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
@@ -224,25 +230,25 @@ hess_f16_lds(const _Float16* __restrict__ X, int64_t ldx, int64_t d, int64_t n_t
     if (diag) wait_later<V2_CPO, V2_NST - 2>(later);
     else wait_later<2 * V2_CPO, V2_NST - 2>(later);
     stage_barrier();
-    // stage s + V2_NST - 1 goes into the buffer read in iteration s - 1; its copies are
-    // spread between the MFMAs so that a stalled copy issue does not leave the matrix core idle
+    // stage s + V2_NST - 1 goes into the buffer read in iteration s - 1; its copies go
+    // between the first MFMAs so that a stalled copy issue does not leave the matrix core idle
     const bool more = s + V2_NST - 1 < nsteps;
     const short* sa = stage_a(s);
     const short* sb = diag ? sa : sa + V2_STAGE_HALFS;
 #pragma unroll
     for (int kk = 0; kk < V2_BK / 16; ++kk) {
-      half8 af[4], bf[4];
+      half8 af[4], bf[V2_BFR];
 #pragma unroll
       for (int a = 0; a < 4; ++a) af[a] = v2_frag(sa, wm * 128 + a * 32, kk * 16, lane);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) bf[b] = v2_frag(sb, wn * 128 + b * 32, kk * 16, lane);
+      for (int b = 0; b < V2_BFR; ++b) bf[b] = v2_frag(sb, wn * 64 + b * 32, kk * 16, lane);
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < V2_BFR; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
-        const int part = kk * 4 + a;   // V2_BK / 4 = 2 V2_CPO slots per stage
-        if (more && (part < V2_CPO || !diag)) issue_part(s + V2_NST - 1, part);
+        const int part = kk * 4 + a;   // V2_BK / 4 slots per stage, the first 2 V2_CPO used
+        if (more && part < 2 * V2_CPO && (part < V2_CPO || !diag)) issue_part(s + V2_NST - 1, part);
       }
     }
   }
@@ -251,11 +257,11 @@ hess_f16_lds(const _Float16* __restrict__ X, int64_t ldx, int64_t d, int64_t n_t
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < V2_BFR; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = wm * 128 + a * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int col = wn * 128 + b * 32 + (lane & 31);
+        const int col = wn * 64 + b * 32 + (lane & 31);
         out[row * TILE + col] = acc[a][b][r];
       }
 }
@@ -414,7 +420,7 @@ hipError_t hessian_launch(const HessPlan& p, float* H, const void* X, int x_dtyp
   {
     ProfScope ps("hessian_mfma", stream);
     if (x_dtype == 0) {
-      hipLaunchKernelGGL(hess_f16_lds, dim3(p.padded_tiles * p.splits), dim3(256), 0, stream,
+      hipLaunchKernelGGL(hess_f16_lds, dim3(p.padded_tiles * p.splits), dim3(64 * V2_WAVES), 0, stream,
                          static_cast<const _Float16*>(X), ldx, p.d, p.n_tok, p.tok_per_split,
                          p.tiles, p.padded_tiles, p.splits, part);
     } else {
