@@ -134,73 +134,74 @@ __device__ __forceinline__ void block_prod(float* C, const float* X, const float
 __device__ __forceinline__ float readlane_f(float v, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
+// v of lane (lane % 32) + 32 hs: one half of the wave copied to both.  v_permlane32_swap with
+// both operands v returns the low half in both halves of its first result and the high half
+// in both halves of its second.
+__device__ __forceinline__ float half_bcast(float v, int hs) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, hs ? p[1] : p[0]);
+}
 
 // One wave: S (symmetric 32 x 32 at sp, only its upper triangle is read) = U U^T, U upper;
 // sp <- G = U^-1 (full block, zeros below the diagonal).  Reverse Gaussian elimination:
 // pivot k removes column k from rows i < k of S (rank-1 Schur update) and the same row
 // operation is applied to R (starting from I), so that R = L^-1 for S = L D L^T with L
 // unit upper; then G = D^-1/2 R.  Pivots are taken in pairs (k, k - 1): with
-// beta = S[k][k-1] / S[k][k], column k - 1 after the first update is c2 - beta c1 and its
-// pivot S[k-1][k-1] - beta S[k][k-1], so both updates are applied from one exchange.
-// Lane (j, h) holds column j and rows 2q + h (q = 0..15) of S and R.  Pair (2t+1, 2t) is
-// register t of half 1 and half 0, and the rows still active are registers q < t in both
-// halves.  Rows 2t+1 and 2t go through LDS in the order pos(i) = 16 (i & 1) + (i >> 1), so
-// that a lane reads its rows as consecutive words.
+// beta = S[k][k-1] / S[k][k], column k - 1 after the first update is
+// u2 = S[:, k-1] - beta S[:, k] and its pivot S[k-1][k-1] - beta S[k][k-1], so the pair is
+// one rank-2 update
+//     S -= S[:, k] S[k, :] / p1 + u2 u2^T / p2,   R -= S[:, k] R[k, :] / p1 + u2 R'[k-1, :] / p2
+// on rows and columns below k - 1 (R' = row k - 1 of R after the first pivot).  S and R are
+// kept in the accumulator layout of v_mfma_f32_32x32x2_f32 (lane (j, h) holds column j,
+// rows 8 (c / 4) + 4 h + c % 4 in register c), so each rank-2 update is one MFMA whose
+// A operand (32 x 2) and B operand (2 x 32) are built per lane from rows k and k - 1.
+// Those two rows sit in one half of the wave; v_permlane32_swap copies them to the other.
 // Returns the smallest k < k_valid whose pivot was not positive and finite, else -1.
-__device__ int diag_factor(float* sp, float* bc, int lane, int k_valid) {
+__device__ int diag_factor(float* sp, int lane, int k_valid) {
   const int j = lane & 31, h = lane >> 5;
-  const int pj = 16 * (j & 1) + (j >> 1);
-  float s[16], r[16], piv[16];   // piv[q]: 1 / sqrt(pivot) of this lane's row 2q + h
+  floatx16 s, r;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int i = 2 * q + h;
-    s[q] = i <= j ? sp[i * LS + j] : sp[j * LS + i];
-    r[q] = (i == j) ? 1.0f : 0.0f;
+  for (int c = 0; c < 16; ++c) {
+    const int i = 8 * (c >> 2) + 4 * h + (c & 3);
+    s[c] = i <= j ? sp[i * LS + j] : sp[j * LS + i];
+    r[c] = (i == j) ? 1.0f : 0.0f;
   }
+  floatx16 pv;    // D^-1/2 of the row of register c
   int bad = -1;
 #pragma unroll
   for (int t = LB / 2 - 1; t >= 0; --t) {
     const int k = 2 * t + 1;
-    const float p1 = readlane_f(s[t], k + 32);      // S[k][k]
-    const float bk = readlane_f(s[t], k - 1 + 32);  // S[k][k-1]
-    const float p2 = readlane_f(s[t], k - 1);       // S[k-1][k-1]
+    const int hs = (t >> 1) & 1;                     // half holding rows k and k - 1
+    const int c1 = 4 * (k >> 3) + (k & 3), c2 = c1 - 1;   // their registers
+    const float p1 = readlane_f(s[c1], k + 32 * hs);      // S[k][k]
+    const float bk = readlane_f(s[c1], k - 1 + 32 * hs);  // S[k][k-1]
+    const float p2 = readlane_f(s[c2], k - 1 + 32 * hs);  // S[k-1][k-1]
+    const float sk = half_bcast(s[c1], hs), sk1 = half_bcast(s[c2], hs);   // S[k][j], S[k-1][j]
+    const float rk = half_bcast(r[c1], hs), rk1 = half_bcast(r[c2], hs);   // R[k][j], R[k-1][j]
     const float rp1 = __builtin_amdgcn_rcpf(p1);
     const float beta = bk * rp1;
     const float p2s = fmaf(-beta, bk, p2);
     const float rp2 = __builtin_amdgcn_rcpf(p2s);
     if (k < k_valid && !(p1 > 0.0f && p1 < 3.0e38f)) bad = k;
     if (k - 1 < k_valid && !(p2s > 0.0f && p2s < 3.0e38f)) bad = k - 1;
-    piv[t] = __builtin_amdgcn_rsqf(h ? p1 : p2s);   // D^-1/2 of this lane's row 2t + h
-    // half 1 publishes row k, half 0 row k - 1 (S masked to columns < k - 1)
-    bc[32 * h + pj] = (j < k - 1) ? s[t] : 0.0f;
-    bc[64 + 32 * h + pj] = r[t];
-    const float rk = bc[96 + pj];
-    const float rk1 = fmaf(-beta, rk, bc[64 + pj]);  // row k-1 of R after pivot k
-    r[t] = h ? r[t] : rk1;
+    const float rk1n = fmaf(-beta, rk, rk1);          // R'[k-1][j]
+    if (h == hs) {
+      pv[c1] = __builtin_amdgcn_rsqf(p1);
+      pv[c2] = __builtin_amdgcn_rsqf(p2s);
+      r[c2] = rk1n;
+    }
     if (t == 0) break;
-    float c1[16], c2[16];
-    const floatx4* v1 = reinterpret_cast<const floatx4*>(bc + 32 + 16 * h);
-    const floatx4* v2 = reinterpret_cast<const floatx4*>(bc + 16 * h);
-#pragma unroll
-    for (int v = 0; v < (t + 3) / 4; ++v) {
-      const floatx4 x1 = v1[v], x2 = v2[v];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { c1[4 * v + e] = x1[e]; c2[4 * v + e] = x2[e]; }
-    }
-    const float cj1 = bc[32 + pj];
-    const float cj2 = fmaf(-beta, cj1, bc[pj]);
-    const float a1 = cj1 * rp1, a2 = cj2 * rp2, g1 = rk * rp1, g2 = rk1 * rp2;
-#pragma unroll
-    for (int q = 0; q < t; ++q) {
-      const float c2s = fmaf(-beta, c1[q], c2[q]);
-      s[q] = fmaf(-c1[q], a1, s[q]);
-      s[q] = fmaf(-c2s, a2, s[q]);
-      r[q] = fmaf(-c1[q], g1, r[q]);
-      r[q] = fmaf(-c2s, g2, r[q]);
-    }
+    const float u2 = fmaf(-beta, sk, sk1);
+    const bool act = j < k - 1;
+    const float a = act ? -(h ? u2 * rp2 : sk * rp1) : 0.0f;   // -A[j][h]
+    const float bs = act ? (h ? u2 : sk) : 0.0f;                // B[h][j] for S
+    const float br = h ? rk1n : rk;                             // B[h][j] for R
+    s = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bs, s, 0, 0, 0);
+    r = __builtin_amdgcn_mfma_f32_32x32x2f32(a, br, r, 0, 0, 0);
   }
 #pragma unroll
-  for (int q = 0; q < 16; ++q) sp[(2 * q + h) * LS + j] = r[q] * piv[q];
+  for (int c = 0; c < 16; ++c) sp[(8 * (c >> 2) + 4 * h + (c & 3)) * LS + j] = r[c] * pv[c];
   return bad;
 }
 
@@ -229,7 +230,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 leaf_factor_invert(float* __restrict__ A, int64_t ld, int64_t off, int n, int* flag) {
   __shared__ float slot[NSLOT * SLOT];
   __shared__ float ubuf[(NLB - 1) * SLOT];
-  __shared__ __attribute__((aligned(16))) float bc[128];
   __shared__ int bad_at;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -274,7 +274,7 @@ leaf_factor_invert(float* __restrict__ A, int64_t ld, int64_t off, int n, int* f
         const float* u = ubuf + p * SLOT;
         block_prod<false, true, true, true>(spp, u, u, lane);
       }
-      const int b = diag_factor(spp, bc, lane, n - LB * p);
+      const int b = diag_factor(spp, lane, n - LB * p);
       if (b >= 0 && lane == 0) bad_at = min(bad_at, LB * p + b);
     } else if (p + 1 < NLB) {
       const int pp = p + 1;                               // update products of step p + 1
