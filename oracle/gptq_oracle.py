@@ -28,6 +28,9 @@ Readings where the pages are silent or garbled (each function names the one it u
       z = round(-xmin / s); degenerate range -> [-1, 1].
   R9  code = clip(round(x/s + z), 0, 2^b - 1), round half to even.
   R13 groups are runs of g consecutive input columns of one row.
+  R15 OBQ's greedy choice is the smallest increase of the row's loss after the OBS
+      compensation, (w_p - quant(w_p))^2 / [H_F^-1]_pp, on the per-channel grid of the
+      original row; equal increases take the smallest index.
   P1  every decision that turns a float into an integer (z and the codes) is taken
       in float32, the precision of the GPU kernels; the state (current weights,
       H, G, errors) stays float64.
@@ -40,6 +43,9 @@ sum(e^2) = Delta H_d Delta^T, Delta = E G, blocked = unblocked, invariance to X
 scaling, GPTQ <= RTN, grid membership, exact ties, pack/unpack and known words;
 dequant_matvec: hand-computed products over known words (INT4, INT3 straddling words,
 INT2), the hand-solved 1x2 layer, and sum_t ||W x_t - y_t||^2 = 1/2 sum_r D_r H D_r^T.
+obq_greedy_quantize (tests/test_oracle_obq.py): a brute-force greedy by least squares on
+the token matrix (order, codes and W^), the literal OBS step in the greedy's own order,
+and H proportional to I giving round-to-nearest.
 No function here is "parity unpinned".
 """
 
@@ -53,7 +59,7 @@ __all__ = [
     "hessian", "damp", "inv_chol_upper", "inv_chol_upper_reversed", "prepare_g",
     "group_params", "quantize_values", "gptq_quantize", "gptq_quantize_obs_literal",
     "rtn_quantize", "dequantize", "layer_loss", "direct_loss", "pack_codes", "unpack_codes",
-    "quant_range", "TIE_TOL", "dequant_matvec",
+    "quant_range", "TIE_TOL", "dequant_matvec", "obq_greedy_quantize",
 ]
 
 TIE_TOL = 1e-3   # a v within this many steps of k + 1/2 is a near-tie (either code accepted)
@@ -298,6 +304,55 @@ def gptq_quantize_obs_literal(W, Hd: np.ndarray, bits: int, group: int, sym: boo
         codes[:, q] = code
         w_hat[:, q] = wq
     return {"codes": codes, "w_hat": w_hat, "W_final": Wc}
+
+
+def obq_greedy_quantize(W, Hd: np.ndarray, bits: int, sym: bool) -> Dict[str, np.ndarray]:
+    """Greedy-order quantization (OBQ), the method GPTQ's fixed order replaces ([Q] GPTQ,
+    first improvement), one grid per output channel.  Tiny layers only: O(d_row d_col^3).
+
+    Each row is independent.  With F the set of not-yet-quantized columns of a row and
+    Hinv_F = inv(H_d[F, F]), quantizing w_p (p in F) and moving the rest of F by the OBS
+    compensation raises the row's loss by (w_p - quant(w_p))^2 / [Hinv_F]_pp; the greedy
+    step quantizes the p in F with the smallest such increase (R15; equal increases: the
+    smallest index), applies that compensation, and drops p from F.  Hinv_F without p
+    follows from Hinv_F by eliminating p:  Hinv_F - Hinv_F[:, p] Hinv_F[p, :] / [Hinv_F]_pp
+    (the inverse of a principal submatrix).  The grid (s, z) of each row comes from its
+    original weights (the per-channel case of R7), so it is the same grid as RTN's and as
+    GPTQ's with group 0.  Codes are decided in float32 (R9, P1).
+
+    Returns codes, scales, zeros [d_row, 1], w_hat, and order [d_row, d_col] (the column
+    quantized at each step).
+    """
+    W = np.asarray(W, dtype=np.float64)
+    d_row, d_col = W.shape
+    Hd = np.asarray(Hd, dtype=np.float64)
+    s_all, z_all, _ = group_params(W, bits, sym)
+    codes = np.zeros((d_row, d_col), np.int64)
+    order = np.zeros((d_row, d_col), np.int64)
+    w_hat = np.zeros((d_row, d_col))
+    Hinv0 = np.linalg.inv(Hd)
+    for r in range(d_row):
+        w = W[r].copy()
+        s, z = s_all[r:r + 1], z_all[r:r + 1]
+        Hinv = Hinv0.copy()
+        free = np.ones(d_col, bool)
+        for step in range(d_col):
+            F = np.nonzero(free)[0]
+            code, _ = quantize_values(w[F], np.repeat(s, F.size), np.repeat(z, F.size), bits)
+            wq = float(s[0]) * (code - z[0]).astype(np.float64)
+            inc = (w[F] - wq) ** 2 / np.diag(Hinv)[F]
+            k = int(np.argmin(inc))              # first minimum: the smallest index
+            p = int(F[k])
+            e = (w[p] - wq[k]) / Hinv[p, p]
+            w[F] -= e * Hinv[F, p]
+            w[p] = wq[k]
+            codes[r, p] = code[k]
+            w_hat[r, p] = wq[k]
+            order[r, step] = p
+            Hinv = Hinv - np.outer(Hinv[:, p], Hinv[p, :]) / Hinv[p, p]
+            free[p] = False
+    return {"codes": codes, "scales": s_all.reshape(-1, 1), "zeros": z_all.reshape(-1, 1),
+            "w_hat": w_hat, "order": order}
 
 
 def rtn_quantize(W, bits: int, group: int, sym: bool) -> Dict[str, np.ndarray]:

@@ -14,7 +14,9 @@ the weights nor the text corpus exist here):
 * channel scales sigma_c = exp(N(0, 0.5^2)) per input channel; optionally a
   seed-chosen fraction of channels is multiplied by a constant (outliers);
 * activations X[t, c] = sigma_c * N(0, 1), token-major [n_tok, d], cast to the
-  layer dtype, drawn in chunks of 4096 tokens, each chunk from its own stream.
+  layer dtype, drawn in chunks of 4096 tokens, each chunk from its own stream;
+* for small comparison layers only, correlated activations: the same channel
+  scales times a rank-r Gaussian mixture plus independent noise (gen_acts_lowrank).
 
 Every stream is numpy PCG64 seeded by SeedSequence(seed, spawn_key=(workload id,
 crc32(tensor name), chunk)), so any chunk can be regenerated on its own.
@@ -108,6 +110,19 @@ def gen_acts(wid: int, xname: str, n_tok: int, d: int, dtype: str = "f16", seed:
         with ThreadPoolExecutor(nthr) as ex:
             list(ex.map(fill, range(n_chunks)))
     return out
+
+
+def gen_acts_lowrank(wid: int, xname: str, n_tok: int, d: int, rank: int,
+                     noise: float = 0.3, dtype: str = "f32", seed: int = 0) -> np.ndarray:
+    """Correlated calibration activations for small comparison layers: X[t, :] =
+    sigma_c * (z_t M + noise * n_t), z_t ~ N(0, I_rank), M [rank, d] and n_t ~ N(0, 1),
+    with the same lognormal channel scales as gen_acts.  Token-major [n_tok, d]; one
+    stream, so only for small n_tok."""
+    sig = channel_sigma(wid, xname, d, seed, 0.0, 1.0)
+    rng = _stream(seed, wid, "LR:" + xname, 0)
+    M = rng.standard_normal((rank, d))
+    x = rng.standard_normal((n_tok, rank)) @ M + noise * rng.standard_normal((n_tok, d))
+    return (x * sig).astype(_np_dtype(dtype))
 
 
 # ----------------------------------------------------------------------------------
