@@ -28,6 +28,11 @@ Readings where the pages are silent or garbled (each function names the one it u
       z = round(-xmin / s); degenerate range -> [-1, 1].
   R9  code = clip(round(x/s + z), 0, 2^b - 1), round half to even.
   R13 groups are runs of g consecutive input columns of one row.
+  R16 AWQ's exponent grid is n evenly spaced points of [0, 1] with both ends (n = 20);
+      s = s_X^alpha is formed in float64 and rounded to float32.
+  R17 s_X is the mean |x| of each input channel over all calibration tokens.
+  R18 AWQ's loss L(s) is the layer objective ||W X - Q(W diag s) diag(s)^-1 X||^2 with the
+      round-to-nearest quantizer of R8/R9 applied to the scaled weights.
   R15 OBQ's greedy choice is the smallest increase of the row's loss after the OBS
       compensation, (w_p - quant(w_p))^2 / [H_F^-1]_pp, on the per-channel grid of the
       original row; equal increases take the smallest index.
@@ -60,6 +65,7 @@ __all__ = [
     "group_params", "quantize_values", "gptq_quantize", "gptq_quantize_obs_literal",
     "rtn_quantize", "dequantize", "layer_loss", "direct_loss", "pack_codes", "unpack_codes",
     "quant_range", "TIE_TOL", "dequant_matvec", "obq_greedy_quantize",
+    "act_absmean", "awq_alphas", "awq_scales", "awq_search",
 ]
 
 TIE_TOL = 1e-3   # a v within this many steps of k + 1/2 is a near-tie (either code accepted)
@@ -372,6 +378,64 @@ def rtn_quantize(W, bits: int, group: int, sym: bool) -> Dict[str, np.ndarray]:
             codes[:, c], _ = quantize_values(W[:, c], s, z, bits)
     w_hat = dequantize(codes, scales, zeros, g)
     return {"codes": codes, "scales": scales, "zeros": zeros, "w_hat": w_hat, "group": g}
+
+
+# --------------------------------------------------------------------------- AWQ search
+
+def act_absmean(X, chunk: int = 4096) -> np.ndarray:
+    """s_X: the mean magnitude of each input channel over the calibration tokens ([Q] AWQ;
+    R17).  X token-major [n_tok, d]; summed in float64 over chunks of tokens."""
+    X = np.asarray(X)
+    n, d = X.shape
+    acc = np.zeros(d)
+    for t0 in range(0, n, chunk):
+        acc += np.abs(X[t0:t0 + chunk].astype(np.float64)).sum(axis=0)
+    return acc / n
+
+
+def awq_alphas(n_grid: int = 20) -> np.ndarray:
+    """The grid of the exponent: n_grid evenly spaced points of [0, 1], both ends included
+    ([Q] AWQ, 20-point grid; R16)."""
+    return np.arange(n_grid, dtype=np.float64) / (n_grid - 1)
+
+
+def awq_scales(sx: np.ndarray, alpha: float) -> np.ndarray:
+    """s = s_X^alpha per input channel ([Q] AWQ), formed in float64 and rounded to float32
+    (the value every later decision sees; R16)."""
+    return np.power(np.asarray(sx, dtype=np.float64), float(alpha)).astype(np.float32)
+
+
+def awq_search(W, H: np.ndarray, sx: np.ndarray, bits: int, group: int, sym: bool,
+               n_grid: int = 20) -> Dict[str, np.ndarray]:
+    """Activation-aware scale search ([Q] AWQ): for each alpha of the grid, scale input
+    channel c of W by s_c = s_X[c]^alpha (the activations are divided by the same s, so the
+    product is unchanged before quantization), quantize W' = W diag(s) to the nearest grid
+    point (rtn_quantize, the quantizer of R8/R9, group parameters from W'), and measure the
+    layer objective for the effective weights Q(W') diag(s)^-1 on the calibration inputs:
+        L(alpha) = ||W X - Q(W') diag(s)^-1 X||^2 = 1/2 sum_r D_r H D_r^T,
+        D = W - Q(W') diag(s)^-1,  H = 2 X X^T undamped (R18).
+    alpha* is the first grid point with the smallest loss.  W' is formed in float32 from the
+    float32 weights and s (the precision of the GPU path, P1).
+
+    Returns alphas, losses [n_grid], best (index), alpha, s (float32 [d_col]), codes, scales,
+    zeros of Q(W') at alpha*, w_hat (the effective weights Q(W') diag(s)^-1) and Wp (W').
+    """
+    W32 = np.asarray(W, dtype=np.float64).astype(np.float32)
+    alphas = awq_alphas(n_grid)
+    losses = np.zeros(n_grid)
+    keep = None
+    for i, a in enumerate(alphas):
+        sc = awq_scales(sx, a)
+        Wp = (W32 * sc[None, :]).astype(np.float32)
+        r = rtn_quantize(Wp, bits, group, sym)
+        w_eff = r["w_hat"] / sc.astype(np.float64)[None, :]
+        losses[i] = layer_loss(W32, w_eff, H)
+        if keep is None or losses[i] < losses[keep[0]]:
+            keep = (i, sc, Wp, r, w_eff)
+    i, sc, Wp, r, w_eff = keep
+    return {"alphas": alphas, "losses": losses, "best": i, "alpha": float(alphas[i]), "s": sc,
+            "codes": r["codes"], "scales": r["scales"], "zeros": r["zeros"], "w_hat": w_eff,
+            "Wp": Wp, "group": r["group"]}
 
 
 # --------------------------------------------------------------------------- a8
