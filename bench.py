@@ -13,7 +13,10 @@ damping 1% of mean diag(H).  Synthetic, seeded inputs (post_weight_quantization_
 
 Also printed: the roofline of the dominant kernel (its per-launch duration from HIP events
 recorded by the library around each launch on the stream it runs on) and the CPU oracle timed
-on a bounded sample of the same workload.
+on a bounded sample of the same workload.  After the timed steps, outside the metric: the
+weight-only quantized product over packed weights (`w4a16`) and AWQ's activation-aware scale
+search on the same layer and tokens (`awq`), with the layer losses of round-to-nearest, of
+AWQ's choice and of the GPTQ output.
 """
 
 import argparse
@@ -42,6 +45,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-w4a16", action="store_true",
                    help="skip the weight-only quantized product leg")
+    p.add_argument("--no-awq", action="store_true",
+                   help="skip the AWQ scale-search leg after the timed steps")
     p.add_argument("--cpu-tokens", type=int, default=16384)
     p.add_argument("--cpu-rows", type=int, default=128)
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -154,6 +159,58 @@ def w4a16_leg(G, torch, dev, layers, reps=100):
                     "n": 1, "avg_launch_us": avg_s * 1e6, "bytes_per_launch": nbytes,
                     "achieved": ach, "peak": PEAK["hbm"], "unit": "GB/s", "frac": ach / PEAK["hbm"]})
     return out
+
+
+def awq_leg(G, torch, Wd, Xd, H, gptq_out, spec, n_grid=20):
+    """AWQ's scale search on the same layer and tokens (gptq_act_absmean over all tokens, then
+    gptq_awq_search over n_grid exponents against the undamped H of the timed steps): wall time
+    of the whole search from events on the launch stream, the loss product against the fp32
+    MFMA roofline (2 d_row d_col^2 flops per grid point), the magnitude pass against HBM, and
+    the layer loss of round-to-nearest (alpha = 0), of the search's choice and of this bench's
+    GPTQ output on the same H."""
+    d_row, d_col = Wd.shape
+    n_tok = Xd.shape[0]
+    dev = Wd.device
+    sx = torch.zeros(d_col, dtype=torch.float64, device=dev)
+    ws_a = torch.empty(max(G.lib().gptq_act_absmean_workspace_size(d_col, n_tok), 256),
+                       dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(G.lib().gptq_awq_workspace_size(d_row, d_col), dtype=torch.uint8,
+                       device=dev)
+
+    def run():
+        sx.zero_()
+        G.act_absmean(sx, Xd, ws=ws_a)
+        return G.awq_search(Wd, H, sx, n_tok, spec, n_grid, ws=ws_s)
+
+    run()
+    torch.cuda.synchronize()
+    G.profile_reset()
+    G.profile_only(None)
+    G.profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    qw, sc, ze, s, losses, best = run()
+    e1.record()
+    torch.cuda.synchronize()
+    G.profile_enable(False)
+    ms = e0.elapsed_time(e1)
+    n_g, ms_g = G.profile_read("awq_gemm")
+    n_a, ms_a = G.profile_read("absmean")
+    n_r, ms_r = G.profile_read("awq_scale_rtn")
+    gemm_tf = 2.0 * d_row * d_col * d_col / (ms_g / n_g / 1e3) / 1e12
+    am_gbs = n_tok * d_col * Xd.element_size() / (ms_a / n_a / 1e3) / 1e9
+    loss_gptq = G.dequant_check(gptq_out[0], gptq_out[1], gptq_out[2], Wd, H, spec)[0].item()
+    lo = losses.cpu().numpy()
+    b = int(best.item())
+    return {"n_grid": n_grid, "ms": ms, "weights_per_s": d_row * d_col / (ms / 1e3),
+            "alpha": b / (n_grid - 1), "loss_rtn": float(lo[0]), "loss_awq": float(lo[b]),
+            "loss_gptq": loss_gptq,
+            "loss_gemm": {"launches": n_g, "avg_launch_ms": ms_g / n_g, "achieved": gemm_tf,
+                          "peak": PEAK["mfma_f32"], "unit": "TFLOP/s",
+                          "frac": gemm_tf / PEAK["mfma_f32"]},
+            "scale_rtn_ms": ms_r,
+            "absmean": {"ms": ms_a / n_a, "achieved": am_gbs, "peak": PEAK["hbm"],
+                        "unit": "GB/s", "frac": am_gbs / PEAK["hbm"]}}
 
 
 def cpu_baseline(W, X_sample, n_tok_full, spec, rows):
@@ -350,6 +407,11 @@ def main():
         w4[-1]["speedup_vs_fp16"] = ref_us / w4[-1]["avg_launch_us"]
         del w16, xb
 
+    # ---- AWQ's activation-aware scale search on the same layer, tokens and H
+    awq = None
+    if not a.no_awq:
+        awq = awq_leg(G, torch, Wd, Xd, H, (qweight, scales, zeros), spec)
+
     cpu = None
     if not a.no_cpu:
         cpu = cpu_baseline(W, X_sample, n_tok, spec_d, min(a.cpu_rows, d_row))
@@ -377,6 +439,7 @@ def main():
         # the column solve alone (G given), from the same profiled step as the phase table
         "quantize_only": {"value": d_row * d_col / (quant_ms / 1e3), "unit": "weights/s"},
         "w4a16": w4,
+        "awq": awq,
         "input_gen_s": gen_s,
     }
     print(json.dumps(out))

@@ -176,10 +176,51 @@ int gptq_dequant_matvec(const uint32_t* qweight, const float* scales, const uint
                         int x_dtype, int64_t n, int64_t ldx, float* y, int64_t ldy,
                         void* stream);
 
+/* ---------------------------------------------------------------- AWQ scale search
+ * Activation-aware scales (page "量化", section AWQ): channel c of W is multiplied by
+ * s_c = s_X[c]^alpha before round-to-nearest quantization and the layer's activations are
+ * meant to be divided by s_c, where s_X is the mean magnitude of each input channel over
+ * the calibration tokens; alpha is the point of the grid k / (n_grid - 1), k = 0..n_grid-1
+ * (n_grid = 20 on the page), with the smallest layer loss
+ *     L = ||W X - Q(W diag s) diag(s)^-1 X||_F^2 = 1/2 sum_r D_r H D_r^T,
+ *     D = W - Q(W diag s) diag(s)^-1,  H = 2 X X^T undamped.
+ * Q is round-to-nearest per row and group of the scaled weights, with the scale and zero
+ * point rules of gptq_quantize_layer (no error compensation).
+ *
+ * gptq_act_absmean: sx_sum[c] += sum_t |X[t][c]| over n_tok token-major rows of X
+ *   (x_dtype F16 or F32, row stride ldx >= d, X and its rows 16-byte aligned), in double.
+ *   The caller zeroes sx_sum and may call once per chunk of tokens; the per-call order of
+ *   the sums is fixed, so results are reproducible.  n_tok = 0 is a no-op.
+ *   Workspace: gptq_act_absmean_workspace_size(d, n_tok) bytes, 256-byte aligned.
+ * gptq_awq_search: s_X = sx_sum / n_tok (n_tok = the number of tokens summed).
+ *   W       [d_row x d_col] F16 or F32, row-major (not modified).
+ *   H       [d_col x d_col] float32 undamped Hessian of the same tokens (both triangles).
+ *   spec    bits, group and sym as for gptq_quantize_layer (group 0 = per output row, else
+ *           a multiple of 16 dividing d_col); block and damp_frac are not used.
+ *   n_grid  2 .. 1000.
+ *   Outputs (device): qweight [d_row x d_col*bits/32], scales and zeros [d_row x d_col/g]
+ *           of Q(W diag s) at the chosen alpha, in gptq_quantize_layer's format (so
+ *           gptq_dequant_matvec applies, with x divided by s); s_out [d_col] float32, the
+ *           chosen s; losses [n_grid] double, L at every grid point; best NULL or 1 int32,
+ *           the chosen grid index (the first smallest loss).
+ *   Workspace: gptq_awq_workspace_size(d_row, d_col) bytes, 256-byte aligned.
+ *   Nothing is read back to the host: the call is asynchronous on the stream.
+ * Errors: GPTQ_EINVAL (shapes, spec, n_grid, NULL pointers, alignment), GPTQ_ENOWS,
+ * GPTQ_EHIP. */
+size_t gptq_act_absmean_workspace_size(int64_t d, int64_t n_tok);
+int gptq_act_absmean(double* sx_sum, int64_t d, const void* X, int x_dtype, int64_t n_tok,
+                     int64_t ldx, void* ws, size_t ws_bytes, void* stream);
+size_t gptq_awq_workspace_size(int64_t d_row, int64_t d_col);
+int gptq_awq_search(const void* W, int w_dtype, int64_t d_row, int64_t d_col, const float* H,
+                    const double* sx_sum, int64_t n_tok, const gptq_spec* spec, int n_grid,
+                    uint32_t* qweight, float* scales, uint8_t* zeros, float* s_out,
+                    double* losses, int32_t* best, void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- instrumentation
  * Optional per-kernel timing with HIP events recorded on the caller's stream around
  * every launch of the named kernel family ("hessian_mfma", "hessian_reduce", "prep_leaf",
- * "prep_gemm", "quant_block", "lazy_gemm", "dequant_matvec", ...).  Enabling costs two event records per
+ * "prep_gemm", "quant_block", "lazy_gemm", "dequant_matvec", "absmean", "awq_scale_rtn",
+ * "awq_gemm", ...).  Enabling costs two event records per
  * timed launch; gptq_profile_only(name) restricts timing to one family (NULL: all).
  * gptq_profile_read returns the number of timed launches and their summed duration in
  * milliseconds (waits for the recorded events).  For measurement, not for production. */

@@ -30,7 +30,8 @@ Readings where the pages are silent or garbled (each function names the one it u
   R13 groups are runs of g consecutive input columns of one row.
   R16 AWQ's exponent grid is n evenly spaced points of [0, 1] with both ends (n = 20);
       s = s_X^alpha is formed in float64 and rounded to float32.
-  R17 s_X is the mean |x| of each input channel over all calibration tokens.
+  R17 s_X is the mean |x| of each input channel over all calibration tokens; a channel
+      with s_X = 0 keeps s = 1.
   R18 AWQ's loss L(s) is the layer objective ||W X - Q(W diag s) diag(s)^-1 X||^2 with the
       round-to-nearest quantizer of R8/R9 applied to the scaled weights.
   R15 OBQ's greedy choice is the smallest increase of the row's loss after the OBS
@@ -401,8 +402,11 @@ def awq_alphas(n_grid: int = 20) -> np.ndarray:
 
 def awq_scales(sx: np.ndarray, alpha: float) -> np.ndarray:
     """s = s_X^alpha per input channel ([Q] AWQ), formed in float64 and rounded to float32
-    (the value every later decision sees; R16)."""
-    return np.power(np.asarray(sx, dtype=np.float64), float(alpha)).astype(np.float32)
+    (the value every later decision sees; R16).  A channel whose activations are all zero
+    keeps s = 1 (R17): it adds nothing to the loss, and 0^alpha would void its weights."""
+    sx = np.asarray(sx, dtype=np.float64)
+    pw = np.power(np.where(sx > 0, sx, 1.0), float(alpha))
+    return np.where(sx > 0, pw, 1.0).astype(np.float32)
 
 
 def awq_search(W, H: np.ndarray, sx: np.ndarray, bits: int, group: int, sym: bool,

@@ -9,7 +9,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgptq.so")
-SOURCES = ["api.hip", "hessian.hip", "gemm.hip", "prep.hip", "quant.hip", "check.hip", "gemv.hip"]
+SOURCES = ["api.hip", "hessian.hip", "gemm.hip", "prep.hip", "quant.hip", "check.hip", "gemv.hip",
+           "awq.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

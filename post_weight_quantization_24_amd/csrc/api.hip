@@ -1,7 +1,7 @@
 // C ABI of libgptq: argument validation (before any HIP call), workspace checks, launch
 // orchestration on the caller's stream, error codes and messages, and the optional
 // per-kernel event timing.  The numerical work lives in hessian.hip, prep.hip,
-// quant.hip, gemm.hip and check.hip.
+// quant.hip, gemm.hip, check.hip, gemv.hip and awq.hip.
 
 #include <cmath>
 #include <cstdarg>
@@ -292,6 +292,69 @@ int gptq_dequant_matvec(const uint32_t* qweight, const float* scales, const uint
   hipError_t e = gptq::matvec_launch(qweight, scales, zeros, d_row, d_col, bits, group, x, n, ldx,
                                      y, ldy, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gptq_dequant_matvec");
+  return GPTQ_OK;
+}
+
+// ---------------------------------------------------------------- AWQ scale search
+size_t gptq_act_absmean_workspace_size(int64_t d, int64_t n_tok) {
+  if (d < 1 || d > (int64_t)1 << 20 || n_tok < 0) return 0;
+  return gptq::absmean_ws_bytes(d, n_tok);
+}
+
+int gptq_act_absmean(double* sx_sum, int64_t d, const void* X, int x_dtype, int64_t n_tok,
+                     int64_t ldx, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (d < 1 || d > (int64_t)1 << 20) return fail(GPTQ_EINVAL, "d out of range (%lld)", (long long)d);
+  if (n_tok < 0) return fail(GPTQ_EINVAL, "n_tok < 0");
+  if (x_dtype != GPTQ_F16 && x_dtype != GPTQ_F32) return fail(GPTQ_EINVAL, "x_dtype must be F16 or F32");
+  if (!sx_sum) return fail(GPTQ_EINVAL, "sx_sum is NULL");
+  if (n_tok == 0) return GPTQ_OK;
+  if (!X) return fail(GPTQ_EINVAL, "X is NULL");
+  if (ldx < d) return fail(GPTQ_EINVAL, "ldx (%lld) < d (%lld)", (long long)ldx, (long long)d);
+  const size_t elt = x_dtype == GPTQ_F16 ? 2 : 4;
+  if (!aligned(X, 16) || (ldx * (int64_t)elt) % 16 != 0)
+    return fail(GPTQ_EINVAL, "X and its rows must be 16-byte aligned");
+  const size_t need = gptq::absmean_ws_bytes(d, n_tok);
+  if (!ws || ws_bytes < need) return fail(GPTQ_ENOWS, "workspace of %zu bytes needed", need);
+  if (!aligned(ws, 256)) return fail(GPTQ_EINVAL, "workspace must be 256-byte aligned");
+  hipError_t e = gptq::absmean_launch(sx_sum, d, X, x_dtype, n_tok, ldx, ws,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gptq_act_absmean");
+  return GPTQ_OK;
+}
+
+size_t gptq_awq_workspace_size(int64_t d_row, int64_t d_col) {
+  if (check_layer(GPTQ_F32, d_row, d_col) != GPTQ_OK) {
+    g_last_error.clear();
+    return 0;
+  }
+  return gptq::awq_ws_bytes(d_row, d_col);
+}
+
+int gptq_awq_search(const void* W, int w_dtype, int64_t d_row, int64_t d_col, const float* H,
+                    const double* sx_sum, int64_t n_tok, const gptq_spec* spec, int n_grid,
+                    uint32_t* qweight, float* scales, uint8_t* zeros, float* s_out,
+                    double* losses, int32_t* best, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  int rc;
+  if ((rc = check_layer(w_dtype, d_row, d_col)) != GPTQ_OK) return rc;
+  if (!spec) return fail(GPTQ_EINVAL, "spec is NULL");
+  if (spec->bits != 2 && spec->bits != 3 && spec->bits != 4 && spec->bits != 8)
+    return fail(GPTQ_EINVAL, "bits must be 2, 3, 4 or 8 (got %d)", spec->bits);
+  if (spec->sym != 0 && spec->sym != 1) return fail(GPTQ_EINVAL, "sym must be 0 or 1");
+  if (spec->group < 0 || (spec->group > 0 && (spec->group % 16 != 0 || d_col % spec->group != 0)))
+    return fail(GPTQ_EINVAL, "group must be 0 or a multiple of 16 dividing d_col (got %d)", spec->group);
+  if (n_grid < 2 || n_grid > 1000) return fail(GPTQ_EINVAL, "n_grid must be in [2, 1000] (got %d)", n_grid);
+  if (n_tok < 1) return fail(GPTQ_EINVAL, "n_tok must be >= 1");
+  if (!W || !H || !sx_sum || !qweight || !scales || !zeros || !s_out || !losses)
+    return fail(GPTQ_EINVAL, "W, H, sx_sum, qweight, scales, zeros, s_out and losses must not be NULL");
+  const size_t need = gptq::awq_ws_bytes(d_row, d_col);
+  if (!ws || ws_bytes < need) return fail(GPTQ_ENOWS, "workspace of %zu bytes needed", need);
+  if (!aligned(ws, 256)) return fail(GPTQ_EINVAL, "workspace must be 256-byte aligned");
+  gptq::AwqArgs a{W, w_dtype, d_row, d_col, H, sx_sum, n_tok, spec->bits, spec->group, spec->sym,
+                  n_grid, qweight, scales, zeros, s_out, losses, best};
+  hipError_t e = gptq::awq_launch(a, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gptq_awq_search");
   return GPTQ_OK;
 }
 

@@ -108,8 +108,15 @@ hipError_t check_launch(const uint32_t* qweight, const float* scales, const uint
                      dim3(256), 0, s, scales, zeros, ng, bits, og);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return loss_of_diff(D, H, d_row, d_col, loss, row_loss, T, rows, s, "check_gemm");
+}
+
+hipError_t loss_of_diff(const float* D, const float* H, int64_t d_row, int64_t d_col, double* loss,
+                        double* row_loss, float* T, double* rows, hipStream_t s,
+                        const char* prof_name) {
   GemmArgs ga{d_row, d_col, d_col, D, d_col, 0, 0, H, d_col, 0, 0, T, d_col, 0, 1.0f, 0.0f};
-  if ((e = gemm_f32(ga, s, "check_gemm")) != hipSuccess) return e;
+  hipError_t e = gemm_f32(ga, s, prof_name);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(row_loss_k, dim3((unsigned)ceil_div(d_row, 4)), dim3(256), 0, s, T, D, d_row,
                      d_col, rows);
   hipLaunchKernelGGL(sum_rows, dim3(1), dim3(256), 0, s, rows, d_row, loss, row_loss);

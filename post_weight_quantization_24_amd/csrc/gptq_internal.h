@@ -78,6 +78,25 @@ hipError_t check_launch(const uint32_t* qweight, const float* scales, const uint
                         int bits, int group, double* loss, double* row_loss, float* W_hat,
                         int64_t* off_grid, void* ws, hipStream_t stream);
 
+// loss = 1/2 sum_r D_r H D_r^T (and its rows) for D [d_row x d_col]; T [d_row x d_col] and
+// rows [d_row] are scratch.  Sums in double, in a fixed order.
+hipError_t loss_of_diff(const float* D, const float* H, int64_t d_row, int64_t d_col, double* loss,
+                        double* row_loss, float* T, double* rows, hipStream_t s,
+                        const char* prof_name);
+
+// ---------------------------------------------------------------- AWQ scale search (awq.hip)
+size_t absmean_ws_bytes(int64_t d, int64_t n_tok);
+hipError_t absmean_launch(double* sx_sum, int64_t d, const void* X, int x_dtype, int64_t n_tok,
+                          int64_t ldx, void* ws, hipStream_t stream);
+size_t awq_ws_bytes(int64_t d_row, int64_t d_col);
+struct AwqArgs {
+  const void* W; int w_dtype; int64_t d_row, d_col;
+  const float* H; const double* sx_sum; int64_t n_tok;
+  int bits, group, sym, n_grid;
+  uint32_t* qweight; float* scales; uint8_t* zeros; float* s_out; double* losses; int* best;
+};
+hipError_t awq_launch(const AwqArgs& a, void* ws, hipStream_t stream);
+
 // ---------------------------------------------------------------- weight-only product (gemv.hip)
 // y[n x d_row] = x[n x d_col] (fp16) * W^T with W^ = s (code - z) read from the packed format.
 int64_t matvec_max_rows_per_launch(int64_t d_col);

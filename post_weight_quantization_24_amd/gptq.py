@@ -53,6 +53,11 @@ _SIGS = {
                             _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "gptq_dequant_matvec": ([_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _int, _i64, _i64, _vp,
                              _i64, _vp], _int),
+    "gptq_act_absmean_workspace_size": ([_i64, _i64], _sz),
+    "gptq_act_absmean": ([_vp, _i64, _vp, _int, _i64, _i64, _vp, _sz, _vp], _int),
+    "gptq_awq_workspace_size": ([_i64, _i64], _sz),
+    "gptq_awq_search": ([_vp, _int, _i64, _i64, _vp, _vp, _i64, ctypes.POINTER(Spec), _int, _vp,
+                         _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "gptq_profile_enable": ([_int], _int),
     "gptq_profile_only": ([ctypes.c_char_p], _int),
     "gptq_profile_reset": ([], _int),
@@ -215,6 +220,41 @@ def dequant_matvec(qweight, scales, zeros, x, bits: int, group: int, d_col: int,
                                      x.stride(0), y.data_ptr(), y.stride(0),
                                      _stream_handle(stream)))
     return y
+
+
+def act_absmean(sx_sum, X, ws=None, stream=None):
+    """sx_sum [d] float64 += sum over the rows of X [n_tok, d] of |x| (gptq_act_absmean)."""
+    d = sx_sum.shape[0]
+    assert X.dim() == 2 and X.shape[1] == d and X.stride(1) == 1 and sx_sum.is_contiguous()
+    n_tok = X.shape[0]
+    ws = _workspace(lib().gptq_act_absmean_workspace_size(d, n_tok), X.device, ws)
+    _check(lib().gptq_act_absmean(sx_sum.data_ptr(), d, X.data_ptr(), _dtype_code(X), n_tok,
+                                  X.stride(0), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                  _stream_handle(stream)))
+    return sx_sum
+
+
+def awq_search(W, H, sx_sum, n_tok: int, spec: Spec, n_grid: int = 20, ws=None, stream=None):
+    """Returns (qweight, scales, zeros, s [d_col] float32, losses [n_grid] float64,
+    best int32[1]) of gptq_awq_search."""
+    torch = _torch()
+    d_row, d_col = W.shape
+    assert W.is_contiguous() and H.is_contiguous() and H.shape == (d_col, d_col)
+    g = d_col if spec.group == 0 else spec.group
+    dev = W.device
+    qweight = torch.empty((d_row, d_col * spec.bits // 32), dtype=torch.int32, device=dev)
+    scales = torch.empty((d_row, d_col // g), dtype=torch.float32, device=dev)
+    zeros = torch.empty((d_row, d_col // g), dtype=torch.uint8, device=dev)
+    s = torch.empty(d_col, dtype=torch.float32, device=dev)
+    losses = torch.empty(n_grid, dtype=torch.float64, device=dev)
+    best = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = _workspace(lib().gptq_awq_workspace_size(d_row, d_col), dev, ws)
+    _check(lib().gptq_awq_search(W.data_ptr(), _dtype_code(W), d_row, d_col, H.data_ptr(),
+                                 sx_sum.data_ptr(), int(n_tok), ctypes.byref(spec), int(n_grid),
+                                 qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                                 s.data_ptr(), losses.data_ptr(), best.data_ptr(), ws.data_ptr(),
+                                 ws.numel() * ws.element_size(), _stream_handle(stream)))
+    return qweight, scales, zeros, s, losses, best
 
 
 def profile_enable(on=True):

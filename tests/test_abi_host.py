@@ -144,3 +144,47 @@ def test_matvec_validation(lib):
     assert f(None, *ok[1:], None) == G.EINVAL
     assert f(*ok[:11], None, 64, None) == G.EINVAL
     assert f(ctypes.c_void_p(0x10004), *ok[1:], None) == G.EINVAL       # qweight alignment
+
+
+def test_absmean_validation(lib):
+    f = lib.gptq_act_absmean
+    ws = lib.gptq_act_absmean_workspace_size(64, 1000)
+    assert ws >= 64 * 8                           # at least one split of float64 sums
+    assert f(FAKE, 0, FAKE, 0, 10, 8, FAKE, ws, None) == G.EINVAL
+    assert f(None, 64, FAKE, 0, 10, 64, FAKE, ws, None) == G.EINVAL
+    assert f(FAKE, 64, FAKE, 2, 10, 64, FAKE, ws, None) == G.EINVAL              # dtype
+    assert f(FAKE, 64, None, 0, 10, 64, FAKE, ws, None) == G.EINVAL
+    assert f(FAKE, 64, FAKE, 0, 10, 32, FAKE, ws, None) == G.EINVAL              # ldx < d
+    assert f(FAKE, 64, ctypes.c_void_p(0x10008), 0, 10, 64, FAKE, ws, None) == G.EINVAL
+    assert f(FAKE, 60, FAKE, 0, 10, 60, FAKE, ws, None) == G.EINVAL              # row not 16B
+    assert f(FAKE, 64, FAKE, 0, 1000, 64, FAKE, 8, None) == G.ENOWS
+    assert f(FAKE, 64, FAKE, 0, 1000, 64, ctypes.c_void_p(0x10010), ws, None) == G.EINVAL
+    assert f(FAKE, 64, FAKE, 0, 0, 64, None, 0, None) == G.OK                    # no tokens
+
+
+def test_awq_validation(lib):
+    f = lib.gptq_awq_search
+    ws = lib.gptq_awq_workspace_size(64, 256)
+    assert ws >= 2 * 64 * 256 * 4 + 64 * 256       # D, T and the codes
+    assert lib.gptq_awq_workspace_size(64, 100) == 0
+
+    def call(spec, n_grid=20, n_tok=100, W=FAKE, wsz=ws, wsp=FAKE, d_col=256, wdt=0):
+        return f(W, wdt, 64, d_col, FAKE, FAKE, n_tok, ctypes.byref(spec) if spec else None,
+                 n_grid, FAKE, FAKE, FAKE, FAKE, FAKE, None, wsp, wsz, None)
+
+    ok = G.Spec.make(4, 128, False)
+    assert call(G.Spec.make(5, 128, False)) == G.EINVAL
+    assert b"bits" in lib.gptq_last_error()
+    assert call(G.Spec.make(4, 24, False)) == G.EINVAL                           # group
+    assert call(G.Spec.make(4, 96, False)) == G.EINVAL                           # 96 !| 256
+    assert call(ok, n_grid=1) == G.EINVAL
+    assert call(ok, n_grid=1001) == G.EINVAL
+    assert call(ok, n_tok=0) == G.EINVAL
+    assert call(None) == G.EINVAL
+    assert call(ok, W=None) == G.EINVAL
+    assert call(ok, d_col=100) == G.EINVAL
+    assert call(ok, wdt=3) == G.EINVAL
+    assert call(ok, wsz=ws - 1) == G.ENOWS
+    assert call(ok, wsp=ctypes.c_void_p(0x10010)) == G.EINVAL
+    # block and damp_frac are not used by the search
+    assert call(G.Spec.make(4, 128, False, block=7, damp_frac=-1.0), wsz=ws - 1) == G.ENOWS
