@@ -1,0 +1,102 @@
+"""Degenerate and boundary cases of the column solve on the GPU, against the oracle:
+all-zero groups and rows (the [-1, 1] range of the asymmetric rule, amax -> 1 of the
+symmetric rule), a single output row at the smallest width, group = d_col against the
+per-channel form, and values that sit exactly on rounding ties (round half to even).
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+from post_weight_quantization_24_amd import gptq as G
+from tests.parity import compare
+from tests.test_gpu_parity import _torch, codes_of, say, to_dev, weight, _workload_h
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("bits,group,sym,block", [(4, 32, 0, 64), (3, 0, 1, 128), (2, 64, 0, 32)])
+def test_degenerate_groups(bits, group, sym, block):
+    torch = _torch()
+    say("degenerate groups", bits, group, sym, block)
+    d_row, d_col = 48, 256
+    W = weight(940, "deg", d_row, d_col, "f32")
+    W[3] = 0.0                          # a whole zero row
+    W[5, 32:96] = 0.0                   # zero groups inside a row
+    W[7] = 0.01                         # a constant row: the asymmetric range is [0, 0.01]
+    W[9, :128] = -0.02
+    H = _workload_h(d_col, 4 * d_col, wid=941)
+    G32 = O.prepare_g(H, 0.01).astype(np.float32)
+    spec = G.Spec.make(bits, group, sym, block, 0.01)
+    qw, sc, ze, _ = G.quantize_layer(to_dev(W), to_dev(G32), spec)
+    torch.cuda.synchronize()
+    st = compare(W, G32.astype(np.float64), dict(bits=bits, group=group, sym=sym),
+                 codes_of(qw, bits, d_col), sc.cpu().numpy(), ze.cpu().numpy(), H=H, block=block)
+    st.pop("fol")
+    say("stats", st)
+    # the all-zero row quantizes to zero exactly on either rule
+    g = d_col if group == 0 else group
+    wh = O.dequantize(codes_of(qw, bits, d_col), sc.cpu().numpy(), ze.cpu().numpy(), g)
+    assert np.all(wh[3] == 0.0)
+
+
+@pytest.mark.parametrize("d_col,group,block", [(32, 0, 32), (32, 16, 32), (4096, 0, 128)])
+def test_single_row(d_col, group, block):
+    torch = _torch()
+    say("single row", d_col, group, block)
+    W = weight(942, "one%d" % d_col, 1, d_col, "f16")
+    H = _workload_h(d_col, 4 * d_col if d_col < 1024 else 8192, wid=943)
+    G32 = O.prepare_g(H, 0.01).astype(np.float32)
+    spec = G.Spec.make(4, group, 0, block, 0.01)
+    qw, sc, ze, _ = G.quantize_layer(to_dev(W), to_dev(G32), spec)
+    torch.cuda.synchronize()
+    st = compare(W, G32.astype(np.float64), dict(bits=4, group=group, sym=0),
+                 codes_of(qw, 4, d_col), sc.cpu().numpy(), ze.cpu().numpy(), H=H, block=block)
+    st.pop("fol")
+    say("stats", st)
+
+
+def test_group_equal_to_width_is_per_channel():
+    torch = _torch()
+    say("group = d_col against group 0")
+    d_row, d_col = 64, 256
+    W = to_dev(weight(944, "gw", d_row, d_col, "f16"))
+    H = _workload_h(d_col, 1024, wid=945)
+    Gd = to_dev(O.prepare_g(H, 0.01).astype(np.float32))
+    a = G.quantize_layer(W, Gd, G.Spec.make(3, 0, 0, 128))
+    b = G.quantize_layer(W, Gd, G.Spec.make(3, 256, 0, 128))
+    torch.cuda.synchronize()
+    for x, y in zip(a[:3], b[:3]):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("sym", [1, 0])
+def test_exact_ties_round_half_even(sym):
+    """With G diagonal there is no compensation, so every value the quantizer sees is the
+    stored weight.  Rows are built so that w / s + z lands exactly on k + 1/2."""
+    torch = _torch()
+    say("exact ties", sym)
+    d_row, d_col, bits = 16, 64, 4
+    rng = np.random.default_rng(946)
+    W = np.zeros((d_row, d_col), np.float32)
+    for r in range(d_row):
+        if sym:
+            # s = amax / 7 = 1 exactly; codes k - 8 + 1/2 with k + 1/2 inside [-7, 7]
+            W[r] = rng.integers(-7, 7, d_col) + 0.5
+            W[r, 0] = 7.0
+        else:
+            # range [0, 15] gives s = 1 and z = 0; values k + 1/2 in [0.5, 14.5]
+            W[r] = rng.integers(0, 15, d_col) + 0.5
+            W[r, 0], W[r, 1] = 0.0, 15.0
+    G32 = np.diag(np.full(d_col, 0.25, np.float32))
+    spec = G.Spec.make(bits, 0, sym, 64)
+    qw, sc, ze, _ = G.quantize_layer(to_dev(W), to_dev(G32), spec)
+    torch.cuda.synchronize()
+    r = O.rtn_quantize(W, bits, 0, sym)
+    assert np.all(sc.cpu().numpy() == 1.0)
+    np.testing.assert_array_equal(codes_of(qw, bits, d_col), r["codes"])
+    # half to even: the stored code of k + 1/2 (+ z) is the even neighbour
+    v = W.astype(np.float64) + (8 if sym else 0)
+    ties = np.abs(v - np.floor(v) - 0.5) == 0
+    assert ties.sum() > d_row * d_col // 2
+    assert np.all(r["codes"][ties] % 2 == 0)
