@@ -157,8 +157,12 @@ __device__ __forceinline__ float half_bcast(float v, int hs) {
 // rows 8 (c / 4) + 4 h + c % 4 in register c), so each rank-2 update is one MFMA whose
 // A operand (32 x 2) and B operand (2 x 32) are built per lane from rows k and k - 1.
 // Those two rows sit in one half of the wave; v_permlane32_swap copies them to the other.
+// When u is given, the last Schur update S -= U U^T (U = the 32 x 32 block at u) is applied
+// in registers first, by the same MFMA sequence as block_prod: its result is symmetric bit for
+// bit (entries (i, j) and (j, i) sum the same products in the same order), so the mirrored
+// upper triangle plus this update equals updating S in LDS and mirroring afterwards.
 // Returns the smallest k < k_valid whose pivot was not positive and finite, else -1.
-__device__ int diag_factor(float* sp, int lane, int k_valid) {
+__device__ int diag_factor(float* sp, const float* u, int lane, int k_valid) {
   const int j = lane & 31, h = lane >> 5;
   floatx16 s, r;
 #pragma unroll
@@ -166,6 +170,14 @@ __device__ int diag_factor(float* sp, int lane, int k_valid) {
     const int i = 8 * (c >> 2) + 4 * h + (c & 3);
     s[c] = i <= j ? sp[i * LS + j] : sp[j * LS + i];
     r[c] = (i == j) ? 1.0f : 0.0f;
+  }
+  if (u) {
+    float uv[LB / 2];
+#pragma unroll
+    for (int kk = 0; kk < LB / 2; ++kk) uv[kk] = u[j * LS + 2 * kk + h];
+#pragma unroll
+    for (int kk = 0; kk < LB / 2; ++kk)
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(-uv[kk], uv[kk], s, 0, 0, 0);
   }
   floatx16 pv;    // D^-1/2 of the row of register c
   int bad = -1;
@@ -270,11 +282,8 @@ leaf_factor_invert(float* __restrict__ A, int64_t ld, int64_t off, int n, int* f
     const float* gpp = slot + slot_of(p, p) * SLOT;
     if (wave == 0) {
       float* spp = slot + slot_of(p, p) * SLOT;
-      if (p + 1 < NLB) {                                  // S_pp -= U_p U_p^T
-        const float* u = ubuf + p * SLOT;
-        block_prod<false, true, true, true>(spp, u, u, lane);
-      }
-      const int b = diag_factor(spp, lane, n - LB * p);
+      // S_pp -= U_p U_p^T (from the panel of p + 1), then the factorization
+      const int b = diag_factor(spp, p + 1 < NLB ? ubuf + p * SLOT : nullptr, lane, n - LB * p);
       if (b >= 0 && lane == 0) bad_at = min(bad_at, LB * p + b);
     } else if (p + 1 < NLB) {
       const int pp = p + 1;                               // update products of step p + 1
