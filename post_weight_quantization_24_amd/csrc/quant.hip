@@ -237,31 +237,52 @@ quant_block(const float* __restrict__ Wc, const float* __restrict__ G, int64_t d
   float* rinv = smem + g_lds_floats<B>();    // 1 / G_qq
   uint8_t* cbuf = reinterpret_cast<uint8_t*>(rinv + B);  // codes [ROWS_PER_WG][B]
 
+  const int c = threadIdx.x % LPR;
+  const int rl = threadIdx.x / LPR;  // row within the workgroup
+  const int64_t row = (int64_t)blockIdx.x * ROWS_PER_WG + rl;
+  const bool row_ok = row < d_row;
+  // This thread's weights first: their loads stay in flight while G is staged.
+  Row<B> r;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int k = s * LPR + c;
+    r.w[s] = (row_ok && k < width) ? Wc[row * d_col + j0 + k] : 0.0f;
+  }
+  float g_sc = 1.0f, g_z = 0.0f;
+  if (g > B && row_ok) {
+    const int64_t gi = j0 / g;
+    g_sc = scales[row * n_groups + gi];
+    g_z = (float)zeros[row * n_groups + gi];
+  }
+
   // Stage G[j0 + q][j0 + s*16 + c] / G_qq for columns > q (0 elsewhere).  Thread (q0, c)
-  // handles rows q = q0 + 16 i; row q keeps slots i..S-1, so every index is known at
-  // compile time and the loads of up to four rows are in flight together.
-  for (int q = threadIdx.x; q < B; q += 256)
-    rinv[q] = q < width ? 1.0f / G[(j0 + q) * d_col + j0 + q] : 0.0f;
-  __syncthreads();
+  // handles rows q = q0 + 16 i and reads their diagonal entries itself; row q keeps slots
+  // i..S-1, so every index is known at compile time and the loads of all its rows (up to
+  // eight) are in flight together.  1 / G_qq also goes to LDS for the epilogue.
   {
-    const int q0 = threadIdx.x / LPR, c = threadIdx.x % LPR;
+    const int q0 = threadIdx.x / LPR;
     const float* gsrc = G + (j0 + q0) * d_col + j0 + c;
-    constexpr int RPC = S < 4 ? S : (S > 8 ? 2 : 4);   // rows per chunk (bounded registers)
+    constexpr int RPC = S <= 8 ? S : 2;   // rows per chunk (bounded registers)
 #pragma unroll
     for (int i0 = 0; i0 < S; i0 += RPC) {
       float v[RPC][S];
-#pragma unroll
-      for (int i = i0; i < i0 + RPC; ++i)
-#pragma unroll
-        for (int s = i; s < S; ++s) {
-          const int q = q0 + LPR * i, k = s * LPR + c;
-          v[i - i0][s] = (k > q && k < width && q < width)
-                             ? gsrc[(int64_t)LPR * i * d_col + s * LPR] : 0.0f;
-        }
+      float gd[RPC];
 #pragma unroll
       for (int i = i0; i < i0 + RPC; ++i) {
         const int q = q0 + LPR * i;
-        const float rq = rinv[q];
+        gd[i - i0] = q < width ? G[(j0 + q) * d_col + j0 + q] : 1.0f;
+#pragma unroll
+        for (int s = i; s < S; ++s) {
+          const int k = s * LPR + c;
+          v[i - i0][s] = (k > q && k < width && q < width)
+                             ? gsrc[(int64_t)LPR * i * d_col + s * LPR] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int i = i0; i < i0 + RPC; ++i) {
+        const int q = q0 + LPR * i;
+        const float rq = q < width ? 1.0f / gd[i - i0] : 0.0f;
+        if (c == 0) rinv[q] = rq;
         float* dst = gl + grow_off<B>(q);
 #pragma unroll
         for (int s = i; s < S; ++s) dst[(s - i) * LPR + c] = v[i - i0][s] * rq;
@@ -269,22 +290,10 @@ quant_block(const float* __restrict__ Wc, const float* __restrict__ G, int64_t d
     }
   }
 
-  const int c = threadIdx.x % LPR;
-  const int rl = threadIdx.x / LPR;  // row within the workgroup
-  const int64_t row = (int64_t)blockIdx.x * ROWS_PER_WG + rl;
-  const bool row_ok = row < d_row;
-  Row<B> r;
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const int k = s * LPR + c;
-    r.w[s] = (row_ok && k < width) ? Wc[row * d_col + j0 + k] : 0.0f;
-  }
   if (g > B) {
-    const int64_t gi = j0 / g;
-    const float sc = row_ok ? scales[row * n_groups + gi] : 1.0f;
-    r.p.s = sc;
-    r.p.z = row_ok ? (float)zeros[row * n_groups + gi] : 0.0f;
-    r.p.y = __fdiv_rn(1.0f, sc);
+    r.p.s = g_sc;
+    r.p.z = g_z;
+    r.p.y = __fdiv_rn(1.0f, g_sc);
   } else {
     r.p.s = 1.0f;
     r.p.z = 0.0f;
