@@ -223,6 +223,68 @@ hess_f16_lds(const _Float16* __restrict__ X, int64_t ldx, int64_t d, int64_t n_t
 #pragma unroll
   for (int i = 0; i < V2_NST - 1; ++i)
     if (i < nsteps) issue(i);
+
+  if (diag) {
+    // A diagonal tile needs only its 36 fragments (32 x 32) on or below the diagonal:
+    // (R, C) with C <= R in the 8 x 8 grid (the reduction reads nothing above it).  Each wave
+    // keeps a 128 x 64 rectangle of the usual layout (role (dm, dn)) and skips the MFMAs of
+    // fragments above the diagonal; the roles need 7, 3, 0, 0 (dm = 0) and 8, 8, 7, 3
+    // (dm = 1) fragments.  Waves are placed on the SIMDs round robin (wave w on SIMD w % 4),
+    // so roles are permuted to pair 8 with 0 and 7 with 3 on each SIMD: at most 10 MFMAs per
+    // SIMD and 16 tokens instead of 16.  Only operand A is staged.
+    const int role = (0x17326054u >> (4 * wave)) & 0xf;
+    const int dm = role >> 2, dn = role & 3;
+    uint32_t need = 0;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < V2_BFR; ++b)
+        if (2 * dn + b <= 4 * dm + a) need |= 1u << (a * V2_BFR + b);
+    need = __builtin_amdgcn_readfirstlane(need);
+    for (int s = 0; s < nsteps; ++s) {
+      const int later = nsteps - 1 - s < V2_NST - 2 ? nsteps - 1 - s : V2_NST - 2;
+      wait_later<V2_CPO, V2_NST - 2>(later);
+      stage_barrier();
+      const bool more = s + V2_NST - 1 < nsteps;
+      const short* sa = stage_a(s);
+#pragma unroll
+      for (int kk = 0; kk < V2_BK / 16; ++kk) {
+        if (need) {
+          half8 af[4], bf[V2_BFR];
+#pragma unroll
+          for (int a = 0; a < 4; ++a) af[a] = v2_frag(sa, dm * 128 + a * 32, kk * 16, lane);
+#pragma unroll
+          for (int b = 0; b < V2_BFR; ++b) bf[b] = v2_frag(sa, dn * 64 + b * 32, kk * 16, lane);
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < V2_BFR; ++b)
+              if (need & (1u << (a * V2_BFR + b)))
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int part = kk * 4 + a;
+          if (more && part < V2_CPO) issue_part(s + V2_NST - 1, part);
+        }
+      }
+    }
+    float* out = part + ((int64_t)split * tiles + tile) * (int64_t)TILE * TILE;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < V2_BFR; ++b) {
+        if (!(need & (1u << (a * V2_BFR + b)))) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = dm * 128 + a * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int col = dn * 64 + b * 32 + (lane & 31);
+          out[row * TILE + col] = acc[a][b][r];
+        }
+      }
+    return;
+  }
+
   for (int s = 0; s < nsteps; ++s) {
     // stage s has landed once at most `later` stages issued after it are pending
     // (copies retire in order; V2_CPO per operand per wave and stage)
