@@ -165,7 +165,8 @@ def awq_leg(G, torch, Wd, Xd, H, gptq_out, spec, n_grid=20):
     """AWQ's scale search on the same layer and tokens (gptq_act_absmean over all tokens, then
     gptq_awq_search over n_grid exponents against the undamped H of the timed steps): wall time
     of the whole search from events on the launch stream, the loss product against the fp32
-    MFMA roofline (2 d_row d_col^2 flops per grid point), the magnitude pass against HBM, and
+    MFMA roofline (D times the upper triangle of H: d_row d_col (d_col + 1) flops per grid
+    point), the magnitude pass against HBM, and
     the layer loss of round-to-nearest (alpha = 0), of the search's choice and of this bench's
     GPTQ output on the same H."""
     d_row, d_col = Wd.shape
@@ -197,7 +198,7 @@ def awq_leg(G, torch, Wd, Xd, H, gptq_out, spec, n_grid=20):
     n_g, ms_g = G.profile_read("awq_gemm")
     n_a, ms_a = G.profile_read("absmean")
     n_r, ms_r = G.profile_read("awq_scale_rtn")
-    gemm_tf = 2.0 * d_row * d_col * d_col / (ms_g / n_g / 1e3) / 1e12
+    gemm_tf = float(d_row) * d_col * (d_col + 1) / (ms_g / n_g / 1e3) / 1e12
     am_gbs = n_tok * d_col * Xd.element_size() / (ms_a / n_a / 1e3) / 1e9
     loss_gptq = G.dequant_check(gptq_out[0], gptq_out[1], gptq_out[2], Wd, H, spec)[0].item()
     lo = losses.cpu().numpy()

@@ -10,8 +10,9 @@
 // scaled weights; section 量化基础 of the same page).
 //
 // Per grid point: the scales (one thread per channel), W' = W s, its quantization and D in
-// one pass over W (one wave per row and group), then T = D H on the fp32 MFMA GEMM and the
-// row sums of T .* D in double, shared with the dequantization check.  The argmin stays on
+// one pass over W (one wave per row and group), then the loss from half a product: H is
+// symmetric, so 1/2 D H D^T = sum T .* D - 1/2 sum D^2 diag(H) with T = D U, U the upper
+// triangle of H (the fp32 MFMA GEMM with a triangular operand mask), row sums in double.  The argmin stays on
 // the device; a last pass quantizes at alpha*, and the codes are packed like the column
 // solve's output.  Every decision that yields an integer is taken in float32 with IEEE
 // division, the scales s in double and rounded to float32.
@@ -323,8 +324,8 @@ hipError_t awq_launch(const AwqArgs& a, void* ws, hipStream_t stream) {
                          a.d_col, g, a.bits, a.sym, w.D, nullptr, nullptr, nullptr);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = loss_of_diff(w.D, a.H, a.d_row, a.d_col, a.losses + i, nullptr, w.T, w.rows, stream,
-                          "awq_gemm")) != hipSuccess)
+    if ((e = loss_of_diff_upper(w.D, a.H, a.d_row, a.d_col, a.losses + i, nullptr, w.T, w.rows,
+                                stream, "awq_gemm")) != hipSuccess)
       return e;
   }
   ProfScope ps("awq_scale_rtn", stream);

@@ -83,6 +83,11 @@ hipError_t check_launch(const uint32_t* qweight, const float* scales, const uint
 hipError_t loss_of_diff(const float* D, const float* H, int64_t d_row, int64_t d_col, double* loss,
                         double* row_loss, float* T, double* rows, hipStream_t s,
                         const char* prof_name);
+// The same loss for a symmetric H from half the product: T = D U with U the upper triangle
+// of H (diagonal included), then sum_c T D - 1/2 sum_c D^2 H_cc per row.
+hipError_t loss_of_diff_upper(const float* D, const float* H, int64_t d_row, int64_t d_col,
+                              double* loss, double* row_loss, float* T, double* rows, hipStream_t s,
+                              const char* prof_name);
 
 // ---------------------------------------------------------------- AWQ scale search (awq.hip)
 size_t absmean_ws_bytes(int64_t d, int64_t n_tok);
