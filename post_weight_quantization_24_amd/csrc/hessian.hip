@@ -64,13 +64,13 @@ __device__ __forceinline__ int v2_slot(int row, int chunk) { return chunk ^ (4 *
 
 typedef uint32_t rsrc_t __attribute__((ext_vector_type(4)));
 
-// Work item of a workgroup for the f16 kernel.  Workgroups are dispatched round-robin over
-// the 8 XCDs (id % 8), each with its own L2.  When the split count is a multiple of 8, XCD x
-// owns splits x*S/8 .. (x+1)*S/8 - 1 and runs them one after the other, so that the 32 CUs
-// of an XCD stream the same token range at the same time.  Within a split, lower-triangle
-// tiles are visited by 4 x 4-block super-tiles (row-major over the super-tiles, then over
-// the tiles inside one), so that the tiles in flight on an XCD share few channel blocks.
-// The grid covers the triangle padded to a multiple of 4 blocks; padded tiles exit.
+// Work item of a workgroup for the f16 kernel: splits one after the other (split-major).
+// Within a split, lower-triangle tiles are visited by 4 x 4-block super-tiles (row-major
+// over the super-tiles, then over the tiles inside one), so that the tiles in flight share
+// few channel blocks.  The grid covers the triangle padded to a multiple of 4 blocks; padded
+// tiles exit.  Giving each of the 8 XCDs (workgroups go round robin, id % 8) its own token
+// ranges when the split count is a multiple of 8 was measured 3-5 % slower than this order
+// with the eight-wave kernel (q_proj and 8192-wide layers).
 constexpr int SUPER = 4;
 __device__ __forceinline__ void super_tile_coords(int t, int& i, int& j) {
   // tiles before super-row S: 16 * S(S-1)/2 (off-diagonal) + 10 * S (diagonal)
@@ -90,16 +90,9 @@ __device__ __forceinline__ void super_tile_coords(int t, int& i, int& j) {
 }
 __device__ __forceinline__ void hess_work(int id, int padded_tiles, int splits, int& split,
                                           int& ti, int& tj) {
-  int t;
-  if (splits % 8 == 0) {
-    const int xcd = id % 8, k = id / 8;
-    split = xcd * (splits / 8) + k / padded_tiles;
-    t = k % padded_tiles;
-  } else {
-    split = id / padded_tiles;
-    t = id % padded_tiles;
-  }
-  super_tile_coords(t, ti, tj);
+  (void)splits;
+  split = id / padded_tiles;
+  super_tile_coords(id % padded_tiles, ti, tj);
 }
 
 // One wave-wide 1 KB copy global -> LDS: lane l's 16 bytes at buffer offset voff land at
@@ -451,18 +444,18 @@ HessPlan hessian_plan(int64_t d, int64_t n_tok, int64_t ldx, int x_dtype) {
   // one split's rows must stay below 2^30 bytes (32-bit buffer offsets)
   const int64_t elt = x_dtype == 0 ? 2 : 4;
   const int64_t min_split = ceil_div(n_tok * ldx * elt, (int64_t)1 << 30);
-  // Any split count is allowed: multiples of 8 give each XCD whole token ranges (see
-  // hess_work), other counts run split-major over all XCDs.  The measured difference between
-  // the two mappings is small; what matters is the number of full rounds of workgroups
-  // (136 tiles x 16 splits leaves a half-empty ninth round, 15 splits fill exactly eight).
+  // What matters is the number of full rounds of workgroups (136 tiles x 16 splits leaves a
+  // half-empty ninth round, 15 splits fill exactly eight) against the partial tiles every
+  // split writes and the reduction reads again.  That traffic is fixed per tile while a
+  // tile's work grows with the token count, so its weight is 0.004 per split at 262144
+  // tokens, scaled by 262144 / n_tok (fitted on MI355X at d = 4096 and 8192).
+  const double per_split = 0.004 * 262144.0 / (double)(n_tok > 0 ? n_tok : 1);
   for (int64_t s = min_split; s <= max_split || s == min_split; ++s) {
     if (s > 64 && s > min_split) break;
     const int64_t wgs = p.tiles * s * (x_dtype == 0 ? 1 : 16);
-    const double rounds = (x_dtype == 0 && s % 8 == 0)
-                              ? (double)ceil_div(p.tiles * (s / 8), cus / 8)
-                              : (double)ceil_div(wgs, cus);
+    const double rounds = (double)ceil_div(wgs, cus);
     // time ~ rounds * work per workgroup (1/s), plus partial-tile traffic per split
-    const double cost = rounds / (double)s * (x_dtype == 0 ? 1.0 : 1.0 / 16.0) + 0.004 * (double)s;
+    const double cost = rounds / (double)s * (x_dtype == 0 ? 1.0 : 1.0 / 16.0) + per_split * (double)s;
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
       best = (int)s;
