@@ -9,6 +9,9 @@ Sources (cited by page title and section):
           blocks of B = 128 columns with a lazy batch update, per-channel output.
   [G]   page "大模型常见的量化方式" (psvmc.cn), section "按量化粒度划分" (granularity
         table): per-channel and group-wise (128 elements per group) quantization.
+  [S]   page "大模型常见的量化方式" (psvmc.cn), section "大模型的分层" (the decoder layer:
+        attention q/k/v/o_proj and the MLP gate/up/down_proj, quantized sub-layer by
+        sub-layer).
   [L]   page on LLM quantization (m.youleyou.com), section "二、量化是什么" (the
         [-T, T] -> [-127, 127] mapping) and section "四、量化形式" (linear
         quantization with round() and clip() to [qmin, qmax], scale s, offset z).
@@ -34,6 +37,11 @@ Readings where the pages are silent or garbled (each function names the one it u
       with s_X = 0 keeps s = 1.
   R18 AWQ's loss L(s) is the layer objective ||W X - Q(W diag s) diag(s)^-1 X||^2 with the
       round-to-nearest quantizer of R8/R9 applied to the scaled weights.
+  R19 the MLP of a decoder layer (the page lists gate_proj, up_proj and down_proj of the
+      LLaMA MLP without its formula) is the LLaMA one: down(silu(gate x) * up x), with
+      silu(x) = x sigmoid(x).
+  R20 layer-sequential quantization: down_proj is calibrated on the output of the already
+      quantized gate_proj and up_proj, rounded to float16 like the block's input.
   R15 OBQ's greedy choice is the smallest increase of the row's loss after the OBS
       compensation, (w_p - quant(w_p))^2 / [H_F^-1]_pp, on the per-channel grid of the
       original row; equal increases take the smallest index.
@@ -66,7 +74,7 @@ __all__ = [
     "group_params", "quantize_values", "gptq_quantize", "gptq_quantize_obs_literal",
     "rtn_quantize", "dequantize", "layer_loss", "direct_loss", "pack_codes", "unpack_codes",
     "quant_range", "TIE_TOL", "dequant_matvec", "obq_greedy_quantize",
-    "act_absmean", "awq_alphas", "awq_scales", "awq_search",
+    "act_absmean", "awq_alphas", "awq_scales", "awq_search", "silu", "mlp_forward", "mlp_block",
 ]
 
 TIE_TOL = 1e-3   # a v within this many steps of k + 1/2 is a near-tie (either code accepted)
@@ -440,6 +448,50 @@ def awq_search(W, H: np.ndarray, sx: np.ndarray, bits: int, group: int, sym: boo
     return {"alphas": alphas, "losses": losses, "best": i, "alpha": float(alphas[i]), "s": sc,
             "codes": r["codes"], "scales": r["scales"], "zeros": r["zeros"], "w_hat": w_eff,
             "Wp": Wp, "group": r["group"]}
+
+
+# --------------------------------------------------------------------------- MLP block
+
+def silu(x):
+    """x * sigmoid(x) in float64 (the activation of the LLaMA MLP; R19)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def mlp_forward(X, gate, up, bits: int, group: int, d: int) -> np.ndarray:
+    """The MLP's down_proj input from packed gate_proj and up_proj ([S] decoder layer; R19,
+    R20): Y = silu(X G^T) * (X U^T) with G, U the dequantized weights, in float64, rounded to
+    float16 like the block's own input.  gate and up are (words, scales, zeros) as the column
+    solve writes them; X is token-major [n_tok, d]."""
+    g = d if group == 0 else int(group)
+    Xf = np.asarray(X, dtype=np.float64)
+    Gw = dequantize(unpack_codes(gate[0], bits, d), gate[1], gate[2], g)
+    Uw = dequantize(unpack_codes(up[0], bits, d), up[1], up[2], g)
+    return (silu(Xf @ Gw.T) * (Xf @ Uw.T)).astype(np.float16)
+
+
+def mlp_block(W_gate, W_up, W_down, X, bits: int, group: int, sym: bool, block: int,
+              damp_frac: float) -> Dict[str, object]:
+    """Layer-sequential quantization of the MLP of one decoder layer ([S] decoder layer;
+    [Q] GPTQ, layer by layer): gate_proj and up_proj on the block input X (one shared H),
+    then down_proj on Y = mlp_forward of the quantized gate_proj and up_proj, so the
+    quantized sub-layers produce the next sub-layer's calibration input (R20).
+    Returns the three gptq_quantize results, Y, and each layer's loss on its own input."""
+    H_x = hessian(X)
+    G_x = prepare_g(H_x, damp_frac)
+    rg = gptq_quantize(W_gate, G_x, bits, group, sym, block)
+    ru = gptq_quantize(W_up, G_x, bits, group, sym, block)
+    d = np.asarray(X).shape[1]
+    gate = (pack_codes(rg["codes"], bits), rg["scales"], rg["zeros"])
+    up = (pack_codes(ru["codes"], bits), ru["scales"], ru["zeros"])
+    Y = mlp_forward(X, gate, up, bits, group, d)
+    H_y = hessian(Y)
+    G_y = prepare_g(H_y, damp_frac)
+    rd = gptq_quantize(W_down, G_y, bits, group, sym, block)
+    return {"gate": rg, "up": ru, "down": rd, "Y": Y, "H_x": H_x, "H_y": H_y,
+            "loss_gate": layer_loss(W_gate, rg["w_hat"], H_x),
+            "loss_up": layer_loss(W_up, ru["w_hat"], H_x),
+            "loss_down": layer_loss(W_down, rd["w_hat"], H_y)}
 
 
 # --------------------------------------------------------------------------- a8
