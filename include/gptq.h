@@ -216,11 +216,33 @@ int gptq_awq_search(const void* W, int w_dtype, int64_t d_row, int64_t d_col, co
                     uint32_t* qweight, float* scales, uint8_t* zeros, float* s_out,
                     double* losses, int32_t* best, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- MLP block forward
+ * The input of down_proj when one decoder layer's MLP is quantized layer by layer (page
+ * "大模型常见的量化方式", section on the layers of a large model: gate_proj, up_proj and
+ * down_proj of the LLaMA MLP, read as down(silu(gate x) * up x)):
+ *     Y[t][j] = float16( silu(sum_c X[t][c] G^[j][c]) * sum_c X[t][c] U^[j][c] ),
+ *     silu(a) = a / (1 + exp(-a)),
+ * with G^ and U^ dequantized from the packed gate_proj and up_proj as gptq_quantize_layer
+ * writes them (both [d_ff x d], the same bits and group).  Products in float32 on the
+ * matrix cores, tokens in chunks of 8192.
+ *   X    [n_tok x d] fp16 (x_dtype GPTQ_F16), row stride ldx >= d.
+ *   Y    [n_tok x d_ff] fp16 output, row stride ldy >= d_ff.
+ *   d a multiple of 32; bits 2, 3, 4 or 8; group 0 or a multiple of 16 dividing d.
+ *   Workspace: gptq_mlp_forward_workspace_size(n_tok, d, d_ff) bytes, 256-byte aligned
+ *   (the dequantized weights and one chunk's float32 input and products).
+ * Errors: GPTQ_EINVAL, GPTQ_ENOWS, GPTQ_EHIP. */
+size_t gptq_mlp_forward_workspace_size(int64_t n_tok, int64_t d, int64_t d_ff);
+int gptq_mlp_forward(const void* X, int x_dtype, int64_t n_tok, int64_t d, int64_t ldx,
+                     const uint32_t* qgate, const float* sgate, const uint8_t* zgate,
+                     const uint32_t* qup, const float* sup, const uint8_t* zup, int64_t d_ff,
+                     int bits, int group, void* Y, int64_t ldy, void* ws, size_t ws_bytes,
+                     void* stream);
+
 /* ---------------------------------------------------------------- instrumentation
  * Optional per-kernel timing with HIP events recorded on the caller's stream around
  * every launch of the named kernel family ("hessian_mfma", "hessian_reduce", "prep_leaf",
  * "prep_gemm", "quant_block", "lazy_gemm", "dequant_matvec", "absmean", "awq_scale_rtn",
- * "awq_gemm", ...).  Enabling costs two event records per
+ * "awq_gemm", "mlp_gemm", "mlp_elementwise", ...).  Enabling costs two event records per
  * timed launch; gptq_profile_only(name) restricts timing to one family (NULL: all).
  * gptq_profile_read returns the number of timed launches and their summed duration in
  * milliseconds (waits for the recorded events).  For measurement, not for production. */

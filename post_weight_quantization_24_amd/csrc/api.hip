@@ -1,7 +1,7 @@
 // C ABI of libgptq: argument validation (before any HIP call), workspace checks, launch
 // orchestration on the caller's stream, error codes and messages, and the optional
 // per-kernel event timing.  The numerical work lives in hessian.hip, prep.hip,
-// quant.hip, gemm.hip, check.hip, gemv.hip and awq.hip.
+// quant.hip, gemm.hip, check.hip, gemv.hip, awq.hip and mlp.hip.
 
 #include <cmath>
 #include <cstdarg>
@@ -355,6 +355,39 @@ int gptq_awq_search(const void* W, int w_dtype, int64_t d_row, int64_t d_col, co
                   n_grid, qweight, scales, zeros, s_out, losses, best};
   hipError_t e = gptq::awq_launch(a, ws, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gptq_awq_search");
+  return GPTQ_OK;
+}
+
+// ---------------------------------------------------------------- MLP block forward
+size_t gptq_mlp_forward_workspace_size(int64_t n_tok, int64_t d, int64_t d_ff) {
+  if (n_tok < 1 || d < 32 || d_ff < 1 || d > (int64_t)1 << 20 || d_ff > (int64_t)1 << 20) return 0;
+  return gptq::mlp_ws_bytes(n_tok, d, d_ff);
+}
+
+int gptq_mlp_forward(const void* X, int x_dtype, int64_t n_tok, int64_t d, int64_t ldx,
+                     const uint32_t* qgate, const float* sgate, const uint8_t* zgate,
+                     const uint32_t* qup, const float* sup, const uint8_t* zup, int64_t d_ff,
+                     int bits, int group, void* Y, int64_t ldy, void* ws, size_t ws_bytes,
+                     void* stream) {
+  g_last_error.clear();
+  int rc;
+  if ((rc = check_layer(GPTQ_F16, d_ff, d)) != GPTQ_OK) return rc;
+  if (x_dtype != GPTQ_F16) return fail(GPTQ_EINVAL, "X must be fp16 (GPTQ_F16)");
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
+    return fail(GPTQ_EINVAL, "bits must be 2, 3, 4 or 8 (got %d)", bits);
+  if (group < 0 || (group > 0 && (group % 16 != 0 || d % group != 0)))
+    return fail(GPTQ_EINVAL, "group must be 0 or a multiple of 16 dividing d (got %d)", group);
+  if (n_tok < 0) return fail(GPTQ_EINVAL, "n_tok < 0");
+  if (n_tok == 0) return GPTQ_OK;
+  if (ldx < d || ldy < d_ff) return fail(GPTQ_EINVAL, "ldx >= d and ldy >= d_ff required");
+  if (!X || !qgate || !sgate || !zgate || !qup || !sup || !zup || !Y)
+    return fail(GPTQ_EINVAL, "X, the packed gate and up layers and Y must not be NULL");
+  const size_t need = gptq::mlp_ws_bytes(n_tok, d, d_ff);
+  if (!ws || ws_bytes < need) return fail(GPTQ_ENOWS, "workspace of %zu bytes needed", need);
+  if (!aligned(ws, 256)) return fail(GPTQ_EINVAL, "workspace must be 256-byte aligned");
+  hipError_t e = gptq::mlp_launch(X, n_tok, d, ldx, qgate, sgate, zgate, qup, sup, zup, d_ff, bits,
+                                  group, Y, ldy, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gptq_mlp_forward");
   return GPTQ_OK;
 }
 

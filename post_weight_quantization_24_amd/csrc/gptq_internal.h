@@ -102,6 +102,13 @@ struct AwqArgs {
 };
 hipError_t awq_launch(const AwqArgs& a, void* ws, hipStream_t stream);
 
+// ---------------------------------------------------------------- MLP block forward (mlp.hip)
+size_t mlp_ws_bytes(int64_t n_tok, int64_t d, int64_t d_ff);
+hipError_t mlp_launch(const void* X, int64_t n_tok, int64_t d, int64_t ldx,
+                      const uint32_t* qg, const float* sg, const uint8_t* zg,
+                      const uint32_t* qu, const float* su, const uint8_t* zu, int64_t d_ff,
+                      int bits, int group, void* Y, int64_t ldy, void* ws, hipStream_t s);
+
 // ---------------------------------------------------------------- weight-only product (gemv.hip)
 // y[n x d_row] = x[n x d_col] (fp16) * W^T with W^ = s (code - z) read from the packed format.
 int64_t matvec_max_rows_per_launch(int64_t d_col);

@@ -58,6 +58,9 @@ _SIGS = {
     "gptq_awq_workspace_size": ([_i64, _i64], _sz),
     "gptq_awq_search": ([_vp, _int, _i64, _i64, _vp, _vp, _i64, ctypes.POINTER(Spec), _int, _vp,
                          _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "gptq_mlp_forward_workspace_size": ([_i64, _i64, _i64], _sz),
+    "gptq_mlp_forward": ([_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _int,
+                          _int, _vp, _i64, _vp, _sz, _vp], _int),
     "gptq_profile_enable": ([_int], _int),
     "gptq_profile_only": ([ctypes.c_char_p], _int),
     "gptq_profile_reset": ([], _int),
@@ -255,6 +258,24 @@ def awq_search(W, H, sx_sum, n_tok: int, spec: Spec, n_grid: int = 20, ws=None, 
                                  s.data_ptr(), losses.data_ptr(), best.data_ptr(), ws.data_ptr(),
                                  ws.numel() * ws.element_size(), _stream_handle(stream)))
     return qweight, scales, zeros, s, losses, best
+
+
+def mlp_forward(X, gate, up, bits: int, group: int, Y=None, ws=None, stream=None):
+    """Y [n_tok x d_ff] fp16 = silu(X G^T) * (X U^T) from packed gate and up layers, each
+    (qweight, scales, zeros) as quantize_layer returns them (gptq_mlp_forward)."""
+    torch = _torch()
+    n_tok, d = X.shape
+    d_ff = gate[0].shape[0]
+    assert X.stride(1) == 1 and up[0].shape[0] == d_ff
+    if Y is None:
+        Y = torch.empty((n_tok, d_ff), dtype=torch.float16, device=X.device)
+    ws = _workspace(lib().gptq_mlp_forward_workspace_size(max(n_tok, 1), d, d_ff), X.device, ws)
+    _check(lib().gptq_mlp_forward(X.data_ptr(), _dtype_code(X), n_tok, d, X.stride(0),
+                                  gate[0].data_ptr(), gate[1].data_ptr(), gate[2].data_ptr(),
+                                  up[0].data_ptr(), up[1].data_ptr(), up[2].data_ptr(), d_ff,
+                                  bits, group, Y.data_ptr(), Y.stride(0), ws.data_ptr(),
+                                  ws.numel() * ws.element_size(), _stream_handle(stream)))
+    return Y
 
 
 def profile_enable(on=True):

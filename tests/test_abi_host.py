@@ -188,3 +188,25 @@ def test_awq_validation(lib):
     assert call(ok, wsp=ctypes.c_void_p(0x10010)) == G.EINVAL
     # block and damp_frac are not used by the search
     assert call(G.Spec.make(4, 128, False, block=7, damp_frac=-1.0), wsz=ws - 1) == G.ENOWS
+
+
+def test_mlp_forward_validation(lib):
+    f = lib.gptq_mlp_forward
+    ws = lib.gptq_mlp_forward_workspace_size(100, 256, 512)
+    assert ws >= 2 * 512 * 256 * 4                  # the dequantized gate and up weights
+    assert lib.gptq_mlp_forward_workspace_size(0, 256, 512) == 0
+
+    def call(n=100, d=256, d_ff=512, bits=4, group=128, xdt=0, ldx=256, ldy=512, wsz=ws, X=FAKE):
+        return f(X, xdt, n, d, ldx, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, d_ff, bits, group, FAKE,
+                 ldy, FAKE, wsz, None)
+
+    assert call(bits=5) == G.EINVAL
+    assert call(group=24) == G.EINVAL
+    assert call(group=96) == G.EINVAL              # 96 does not divide 256
+    assert call(d=100, ldx=100) == G.EINVAL        # d not a multiple of 32
+    assert call(xdt=1) == G.EINVAL                 # X must be fp16
+    assert call(ldx=128) == G.EINVAL
+    assert call(ldy=256) == G.EINVAL
+    assert call(X=None) == G.EINVAL
+    assert call(wsz=ws - 1) == G.ENOWS
+    assert call(n=0) == G.OK

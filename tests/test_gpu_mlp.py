@@ -1,0 +1,107 @@
+"""GPU parity of the layer-sequential MLP block (gptq_mlp_forward and the driver
+block.quantize_mlp_block) against the oracle (oracle.mlp_forward, oracle.mlp_block).
+
+Tolerance of the forward pass: the GPU forms a = X G^T and b = X U^T in float32 from the
+float32-rounded dequantized weights (each sum within (d + 4) 2^-24 sum|x w| of the exact
+one), silu with expf (a few ulp), and rounds silu(a) b to float16; the oracle rounds the
+float64 value.  Allowed per output: one float16 ulp of the reference plus
+1.1 |b| e_a + (|a| + 1) e_b + 4e-6 |silu(a) b|, with e_a, e_b those sum bounds.
+
+The chain: gate_proj and up_proj against the oracle with the tie-following comparator (the
+parity bar of the column solve); down_proj's input Y against the oracle's own Y (built from
+the oracle's own codes) within the forward tolerance wherever the gate and up codes agree;
+down_proj's codes with the comparator against the oracle's G of its own Y; every layer loss
+within 0.5 %.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+from post_weight_quantization_24_amd import block as BLK
+from post_weight_quantization_24_amd import gptq as G
+from post_weight_quantization_24_amd import synth
+from tests.parity import compare
+from tests.test_gpu_parity import _torch, codes_of, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _packed(rng, rows, d, bits, group):
+    g = d if group == 0 else group
+    codes = rng.integers(0, 1 << bits, (rows, d))
+    scales = rng.uniform(0.002, 0.02, (rows, d // g)).astype(np.float32)
+    zeros = rng.integers(0, 1 << bits, (rows, d // g)).astype(np.uint8)
+    return O.pack_codes(codes, bits), scales, zeros
+
+
+def _forward_tol(X, gate, up, bits, group, d):
+    g = d if group == 0 else group
+    Xf = X.astype(np.float64)
+    Gw = O.dequantize(O.unpack_codes(gate[0], bits, d), gate[1], gate[2], g)
+    Uw = O.dequantize(O.unpack_codes(up[0], bits, d), up[1], up[2], g)
+    a, b = Xf @ Gw.T, Xf @ Uw.T
+    gam = (d + 4) * 2.0 ** -24
+    ea, eb = gam * (np.abs(Xf) @ np.abs(Gw).T), gam * (np.abs(Xf) @ np.abs(Uw).T)
+    y = O.silu(a) * b
+    ref = y.astype(np.float16).astype(np.float64)
+    ulp = 2.0 ** -10 * np.maximum(np.abs(ref), 2.0 ** -14)
+    return ref, ulp + 1.1 * np.abs(b) * ea + (np.abs(a) + 1.0) * eb + 4e-6 * np.abs(y)
+
+
+@pytest.mark.parametrize("n,d,d_ff,bits,group", [
+    (1000, 256, 384, 4, 128), (9000, 512, 256, 3, 0), (5, 64, 96, 2, 16), (300, 1024, 128, 8, 64)])
+def test_mlp_forward(n, d, d_ff, bits, group):
+    torch = _torch()
+    say("mlp_forward", n, d, d_ff, bits, group)
+    rng = np.random.default_rng(950 + d + bits)
+    gate, up = _packed(rng, d_ff, d, bits, group), _packed(rng, d_ff, d, bits, group)
+    X = synth.gen_acts(950, "mlpx%d" % d, n, d, "f16")
+    dev_pack = lambda p: (to_dev(p[0].view(np.int32)), to_dev(p[1]), to_dev(p[2]))
+    Y = G.mlp_forward(to_dev(X), dev_pack(gate), dev_pack(up), bits, group)
+    torch.cuda.synchronize()
+    got = Y.cpu().numpy().astype(np.float64)
+    ref, tol = _forward_tol(X, gate, up, bits, group, d)
+    err = np.abs(got - ref)
+    say("max err / tol %.3g" % float((err / tol).max()))
+    assert np.all(err <= tol)
+    np.testing.assert_array_equal(ref.astype(np.float16), O.mlp_forward(X, gate, up, bits, group, d))
+
+
+def test_mlp_block_chain():
+    torch = _torch()
+    say("mlp block chain")
+    n, d, d_ff, bits, group, sym, B, damp = 4096, 256, 512, 4, 128, False, 128, 0.01
+    Wg = synth.gen_weight(960, "g", d_ff, d, 0.02, "f16")
+    Wu = synth.gen_weight(960, "u", d_ff, d, 0.02, "f16")
+    Wd = synth.gen_weight(960, "dn", d, d_ff, 0.02, "f16")
+    X = synth.gen_acts(960, "x", n, d, "f16")
+    spec = G.Spec.make(bits, group, sym, B, damp)
+    r = BLK.quantize_mlp_block(to_dev(Wg), to_dev(Wu), to_dev(Wd), to_dev(X), spec)
+    o = O.mlp_block(Wg, Wu, Wd, X, bits, group, sym, B, damp)
+    sd = dict(bits=bits, group=group, sym=sym)
+    G_x = O.prepare_g(o["H_x"], damp)
+    same = True
+    for name, W in (("gate", Wg), ("up", Wu)):
+        q = r[name]
+        codes = codes_of(q[0], bits, d)
+        st = compare(W, G_x, sd, codes, q[1].cpu().numpy(), q[2].cpu().numpy(), H=o["H_x"],
+                     gpu_loss=r["loss_" + name], block=B)
+        st.pop("fol")
+        say(name, st)
+        same = same and np.array_equal(codes, o[name]["codes"])
+    Y = r["Y"].cpu().numpy()
+    if same:
+        gate = (O.pack_codes(o["gate"]["codes"], bits), o["gate"]["scales"], o["gate"]["zeros"])
+        up = (O.pack_codes(o["up"]["codes"], bits), o["up"]["scales"], o["up"]["zeros"])
+        ref, tol = _forward_tol(X, gate, up, bits, group, d)
+        assert np.all(np.abs(Y.astype(np.float64) - ref) <= tol)
+    say("Y identical to the oracle's on %.6f of entries" % float(np.mean(Y == o["Y"])))
+    G_y = O.prepare_g(o["H_y"], damp)
+    q = r["down"]
+    st = compare(Wd, G_y, sd, codes_of(q[0], bits, d_ff), q[1].cpu().numpy(), q[2].cpu().numpy(),
+                 H=o["H_y"], gpu_loss=r["loss_down"], block=B)
+    st.pop("fol")
+    say("down", st)
+    for k in ("loss_gate", "loss_up", "loss_down"):
+        assert abs(r[k] - o[k]) <= 5e-3 * o[k], (k, r[k], o[k])
