@@ -42,6 +42,18 @@ Readings where the pages are silent or garbled (each function names the one it u
       silu(x) = x sigmoid(x).
   R20 layer-sequential quantization: down_proj is calibrated on the output of the already
       quantized gate_proj and up_proj, rounded to float16 like the block's input.
+  R21 the decoder layer (the page lists input_layernorm, self_attn,
+      post_attention_layernorm and mlp of the LLaMA layer, norms kept in float16) is the
+      LLaMA one: h = x + o_proj(attn(rmsnorm1(x))), and the MLP takes rmsnorm2(h).  Every
+      tensor a quantized sub-layer reads (the norm outputs, q/k/v, the attention output O,
+      the residual h, the MLP's Y) is stored in float16; the oracle rounds each float64
+      value once.
+  R22 rmsnorm(x) = x / sqrt(mean(x^2) + eps) * gamma per token, eps = 1e-6.
+  R23 attention is LLaMA's causal multi-head self-attention: heads of 128 channels,
+      rotary position embedding on q and k (theta = 10000, channel i of a head rotated with
+      channel i + 64 by the angle pos * theta^(-2i/128)), positions 0..L-1 within each of
+      the independent sequences the calibration tokens are cut into, softmax of
+      q k^T / sqrt(128) over the keys at or before the query.
   R15 OBQ's greedy choice is the smallest increase of the row's loss after the OBS
       compensation, (w_p - quant(w_p))^2 / [H_F^-1]_pp, on the per-channel grid of the
       original row; equal increases take the smallest index.
@@ -75,6 +87,7 @@ __all__ = [
     "rtn_quantize", "dequantize", "layer_loss", "direct_loss", "pack_codes", "unpack_codes",
     "quant_range", "TIE_TOL", "dequant_matvec", "obq_greedy_quantize",
     "act_absmean", "awq_alphas", "awq_scales", "awq_search", "silu", "mlp_forward", "mlp_block",
+    "rmsnorm", "rope", "causal_attention", "attn_forward", "residual_linear", "decoder_block",
 ]
 
 TIE_TOL = 1e-3   # a v within this many steps of k + 1/2 is a near-tie (either code accepted)
@@ -492,6 +505,103 @@ def mlp_block(W_gate, W_up, W_down, X, bits: int, group: int, sym: bool, block: 
             "loss_gate": layer_loss(W_gate, rg["w_hat"], H_x),
             "loss_up": layer_loss(W_up, ru["w_hat"], H_x),
             "loss_down": layer_loss(W_down, rd["w_hat"], H_y)}
+
+
+# --------------------------------------------------------------------------- attention half
+
+def rmsnorm(x, gamma, eps: float = 1e-6) -> np.ndarray:
+    """Root-mean-square normalization of each token ([S] decoder layer; R21, R22):
+    x / sqrt(mean_c x_c^2 + eps) * gamma in float64, rounded once to float16."""
+    xf = np.asarray(x, dtype=np.float64)
+    r = np.sqrt(np.mean(xf * xf, axis=1, keepdims=True) + eps)
+    return (xf / r * np.asarray(gamma, dtype=np.float64)[None, :]).astype(np.float16)
+
+
+def rope(x, pos, theta: float = 10000.0) -> np.ndarray:
+    """Rotary position embedding of one head's vectors (R23): x [n, hd] float64, pos [n].
+    Channel i (< hd/2) and channel i + hd/2 turn together by pos * theta^(-2i/hd)."""
+    x = np.asarray(x, dtype=np.float64)
+    hd = x.shape[1]
+    half = hd // 2
+    inv = theta ** (-(2.0 * np.arange(half)) / hd)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * inv[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[:, :half], x[:, half:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=1)
+
+
+def causal_attention(q, k, v, seq_len: int, head_dim: int = 128) -> np.ndarray:
+    """Causal multi-head attention over independent sequences (R23), float64 in and out.
+    q, k, v are token-major [n_tok, n_heads * head_dim]; rotary embedding is applied to q
+    and k here; the last sequence may be shorter than seq_len."""
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    n, d = q.shape
+    out = np.zeros((n, d))
+    for t0 in range(0, n, seq_len):
+        t1 = min(n, t0 + seq_len)
+        pos = np.arange(t1 - t0)
+        mask = pos[None, :] <= pos[:, None]
+        for h in range(d // head_dim):
+            cs = slice(h * head_dim, (h + 1) * head_dim)
+            qh, kh = rope(q[t0:t1, cs], pos), rope(k[t0:t1, cs], pos)
+            sc = (qh @ kh.T) / np.sqrt(head_dim)
+            sc = np.where(mask, sc, -np.inf)
+            p = np.exp(sc - sc.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            out[t0:t1, cs] = p @ v[t0:t1, cs]
+    return out
+
+
+def attn_forward(Xn, qp, kp, vp, bits: int, group: int, seq_len: int,
+                 head_dim: int = 128) -> np.ndarray:
+    """o_proj's calibration input from the packed q/k/v_proj ([S] decoder layer; R20, R21,
+    R23): q, k, v = float16 of X W^T, then causal attention, rounded to float16."""
+    d = np.asarray(Xn).shape[1]
+    qkv = [dequant_matvec(p[0], p[1], p[2], bits, group, d, Xn).astype(np.float16)
+           for p in (qp, kp, vp)]
+    return causal_attention(*qkv, seq_len, head_dim).astype(np.float16)
+
+
+def residual_linear(O, x, op, bits: int, group: int) -> np.ndarray:
+    """The residual stream after attention (R21): h = float16(x + O W_o^T)."""
+    d = np.asarray(O).shape[1]
+    y = dequant_matvec(op[0], op[1], op[2], bits, group, d, O)
+    return (np.asarray(x, dtype=np.float64) + y).astype(np.float16)
+
+
+def decoder_block(W: Dict[str, np.ndarray], x, gamma1, gamma2, seq_len: int, bits: int,
+                  group: int, sym: bool, block: int, damp_frac: float,
+                  head_dim: int = 128) -> Dict[str, object]:
+    """Layer-sequential quantization of one decoder layer ([S] decoder layer; [Q] GPTQ,
+    layer by layer; R20, R21): q/k/v_proj on rmsnorm1(x) (one shared H), o_proj on the
+    attention output of the quantized q/k/v, gate/up_proj on rmsnorm2(h) with h the residual
+    through the quantized o_proj, down_proj on the MLP product of the quantized gate/up.
+    W maps the seven sub-layer names to their weights.  Returns each gptq_quantize result,
+    every calibration input and Hessian, and each layer's loss on its own input."""
+    r: Dict[str, object] = {}
+
+    def run(names, X):
+        H = hessian(X)
+        G = prepare_g(H, damp_frac)
+        out = []
+        for nm in names:
+            q = gptq_quantize(W[nm], G, bits, group, sym, block)
+            r[nm] = q
+            r["loss_" + nm] = layer_loss(W[nm], q["w_hat"], H)
+            out.append((pack_codes(q["codes"], bits), q["scales"], q["zeros"]))
+        return H, out
+
+    n1 = rmsnorm(x, gamma1)
+    r["H_n1"], (qp, kp, vp) = run(("q_proj", "k_proj", "v_proj"), n1)
+    O = attn_forward(n1, qp, kp, vp, bits, group, seq_len, head_dim)
+    r["H_o"], (op,) = run(("o_proj",), O)
+    h = residual_linear(O, x, op, bits, group)
+    n2 = rmsnorm(h, gamma2)
+    r["H_n2"], (gp, up) = run(("gate_proj", "up_proj"), n2)
+    Y = mlp_forward(n2, gp, up, bits, group, n2.shape[1])
+    r["H_y"], _ = run(("down_proj",), Y)
+    r.update(n1=n1, O=O, h=h, n2=n2, Y=Y)
+    return r
 
 
 # --------------------------------------------------------------------------- a8

@@ -54,6 +54,12 @@ def gen_weight(wid: int, name: str, d_row: int, d_col: int, sigma: float,
     return w.astype(_np_dtype(dtype))
 
 
+def gen_norm_weight(wid: int, name: str, d: int, dtype: str = "f16", seed: int = 0) -> np.ndarray:
+    """A normalization weight gamma [d] = exp(0.2 N(0, 1)) in the given storage dtype."""
+    rng = _stream(seed, wid, "N:" + name, 0)
+    return np.exp(0.2 * rng.standard_normal(d)).astype(_np_dtype(dtype))
+
+
 def channel_sigma(wid: int, xname: str, d: int, seed: int = 0,
                   outlier_frac: float = 0.0, outlier_scale: float = 100.0) -> np.ndarray:
     """Per-input-channel scale sigma_c (float64): lognormal(0, 0.5), outliers scaled."""
