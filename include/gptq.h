@@ -238,6 +238,55 @@ int gptq_mlp_forward(const void* X, int x_dtype, int64_t n_tok, int64_t d, int64
                      int bits, int group, void* Y, int64_t ldy, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* ---------------------------------------------------------------- attention half of a block
+ * The calibration inputs of q/k/v_proj and o_proj, and the residual that feeds the MLP, when
+ * one decoder layer is quantized layer by layer (page "大模型常见的量化方式", section on the
+ * layers of a large model: the LLaMA layer with input_layernorm, self_attn,
+ * post_attention_layernorm and the MLP, the norms kept in float16).  Read as the LLaMA layer:
+ *
+ * gptq_rmsnorm: y[t][c] = float16( x[t][c] / sqrt(mean_c x[t][c]^2 + eps) * gamma[c] ),
+ *   in float64 (rounded to float32, then float16).
+ *   x, y [n_tok x d] fp16, row strides ldx, ldy >= d; gamma [d] fp16.  d, ldx and ldy
+ *   multiples of 8; x, y and gamma 16-byte aligned; eps finite and >= 0.  In place (y == x,
+ *   ldy == ldx) is allowed.  No workspace.
+ *
+ * gptq_attention_forward: O = float16( attention(rope(q), rope(k), v) ) with
+ *   q, k, v = float16(X W^T) for the packed q_proj, k_proj and v_proj (each [d x d], the
+ *   same bits and group, in gptq_quantize_layer's format; products in float32 on the matrix
+ *   cores).  Causal multi-head self-attention, heads of 128 channels (head h is channels
+ *   [128 h, 128 h + 128)), softmax of q.k / sqrt(128) over the keys at or before the query.
+ *   Rotary embedding: channels i and i + 64 of a head turn by pos * 10000^(-2i/128), angles
+ *   in float64.  The tokens form independent sequences [0, seq_len), [seq_len, 2 seq_len),
+ *   ...; pos counts from 0 in each; the last one may be shorter.
+ *   X  [n_tok x d] fp16, row stride ldx >= d;  O [n_tok x d] fp16, ldo >= d, ldo a multiple
+ *   of 8 and O 16-byte aligned.  d a multiple of 128; bits 2, 3, 4 or 8; group 0 or a
+ *   multiple of 16 dividing d; 1 <= seq_len <= 2^20.
+ *   Workspace: gptq_attention_forward_workspace_size(n_tok, d, seq_len) bytes, 256-byte
+ *   aligned (the dequantized weights, one chunk of whole sequences in float32, the angles).
+ *
+ * gptq_residual_linear: Hout = float16( R + X W^T ) for one packed layer W [d_out x d_in]
+ *   (o_proj: X the attention output, R the block input).
+ *   X [n_tok x d_in] fp16, ldx >= d_in; R and Hout [n_tok x d_out] fp16, ldr, ldh >= d_out.
+ *   d_in a multiple of 32; bits and group as above (group divides d_in).
+ *   Workspace: gptq_residual_linear_workspace_size(n_tok, d_in, d_out) bytes, 256-byte aligned.
+ *
+ * All three are asynchronous on the stream; n_tok = 0 is a no-op.
+ * Errors: GPTQ_EINVAL (shapes, strides, alignment, NULL pointers), GPTQ_ENOWS, GPTQ_EHIP. */
+int gptq_rmsnorm(const void* x, int64_t n_tok, int64_t d, int64_t ldx, const void* gamma,
+                 double eps, void* y, int64_t ldy, void* stream);
+size_t gptq_attention_forward_workspace_size(int64_t n_tok, int64_t d, int64_t seq_len);
+int gptq_attention_forward(const void* X, int64_t n_tok, int64_t d, int64_t ldx,
+                           const uint32_t* qq, const float* sq, const uint8_t* zq,
+                           const uint32_t* qk, const float* sk, const uint8_t* zk,
+                           const uint32_t* qv, const float* sv, const uint8_t* zv, int bits,
+                           int group, int64_t seq_len, void* O, int64_t ldo, void* ws,
+                           size_t ws_bytes, void* stream);
+size_t gptq_residual_linear_workspace_size(int64_t n_tok, int64_t d_in, int64_t d_out);
+int gptq_residual_linear(const void* X, int64_t n_tok, int64_t d_in, int64_t ldx, const void* R,
+                         int64_t ldr, const uint32_t* q, const float* s, const uint8_t* z,
+                         int64_t d_out, int bits, int group, void* Hout, int64_t ldh, void* ws,
+                         size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- instrumentation
  * Optional per-kernel timing with HIP events recorded on the caller's stream around
  * every launch of the named kernel family ("hessian_mfma", "hessian_reduce", "prep_leaf",

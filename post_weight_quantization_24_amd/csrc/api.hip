@@ -391,6 +391,108 @@ int gptq_mlp_forward(const void* X, int x_dtype, int64_t n_tok, int64_t d, int64
   return GPTQ_OK;
 }
 
+static int check_packed(int bits, int group, int64_t d) {
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
+    return fail(GPTQ_EINVAL, "bits must be 2, 3, 4 or 8 (got %d)", bits);
+  if (group < 0 || (group > 0 && (group % 16 != 0 || d % group != 0)))
+    return fail(GPTQ_EINVAL, "group must be 0 or a multiple of 16 dividing %lld (got %d)",
+                (long long)d, group);
+  return GPTQ_OK;
+}
+
+int gptq_rmsnorm(const void* x, int64_t n_tok, int64_t d, int64_t ldx, const void* gamma,
+                 double eps, void* y, int64_t ldy, void* stream) {
+  g_last_error.clear();
+  if (d < 8 || d % 8 != 0 || d > (int64_t)1 << 20)
+    return fail(GPTQ_EINVAL, "d must be a positive multiple of 8 (got %lld)", (long long)d);
+  if (n_tok < 0) return fail(GPTQ_EINVAL, "n_tok < 0");
+  if (!(eps >= 0.0) || !std::isfinite(eps)) return fail(GPTQ_EINVAL, "eps must be finite and >= 0");
+  if (ldx < d || ldy < d || ldx % 8 != 0 || ldy % 8 != 0)
+    return fail(GPTQ_EINVAL, "ldx and ldy must be >= d and multiples of 8");
+  if (n_tok == 0) return GPTQ_OK;
+  if (!x || !gamma || !y) return fail(GPTQ_EINVAL, "x, gamma and y must not be NULL");
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(gamma, 16))
+    return fail(GPTQ_EINVAL, "x, y and gamma must be 16-byte aligned");
+  hipError_t e = gptq::rmsnorm_launch(static_cast<const _Float16*>(x), ldx, n_tok, d,
+                                      static_cast<const _Float16*>(gamma), eps,
+                                      static_cast<_Float16*>(y), ldy,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gptq_rmsnorm");
+  return GPTQ_OK;
+}
+
+size_t gptq_attention_forward_workspace_size(int64_t n_tok, int64_t d, int64_t seq_len) {
+  if (n_tok < 1 || d < gptq::ATTN_HEAD_DIM || d % gptq::ATTN_HEAD_DIM != 0 || d > (int64_t)1 << 16 ||
+      seq_len < 1 || seq_len > (int64_t)1 << 20)
+    return 0;
+  return gptq::attn_ws_bytes(n_tok, d, seq_len);
+}
+
+int gptq_attention_forward(const void* X, int64_t n_tok, int64_t d, int64_t ldx,
+                           const uint32_t* qq, const float* sq, const uint8_t* zq,
+                           const uint32_t* qk, const float* sk, const uint8_t* zk,
+                           const uint32_t* qv, const float* sv, const uint8_t* zv, int bits,
+                           int group, int64_t seq_len, void* O, int64_t ldo, void* ws,
+                           size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  int rc;
+  if (d < gptq::ATTN_HEAD_DIM || d % gptq::ATTN_HEAD_DIM != 0 || d > (int64_t)1 << 16)
+    return fail(GPTQ_EINVAL, "d must be a positive multiple of %d (got %lld)", gptq::ATTN_HEAD_DIM,
+                (long long)d);
+  if ((rc = check_packed(bits, group, d)) != GPTQ_OK) return rc;
+  if (seq_len < 1 || seq_len > (int64_t)1 << 20) return fail(GPTQ_EINVAL, "seq_len out of range");
+  if (n_tok < 0) return fail(GPTQ_EINVAL, "n_tok < 0");
+  if (ldx < d || ldo < d || ldo % 8 != 0)
+    return fail(GPTQ_EINVAL, "ldx >= d, ldo >= d and ldo a multiple of 8 required");
+  if (n_tok == 0) return GPTQ_OK;
+  if (!X || !qq || !sq || !zq || !qk || !sk || !zk || !qv || !sv || !zv || !O)
+    return fail(GPTQ_EINVAL, "X, the packed q/k/v layers and O must not be NULL");
+  if (!aligned(O, 16)) return fail(GPTQ_EINVAL, "O must be 16-byte aligned");
+  const size_t need = gptq::attn_ws_bytes(n_tok, d, seq_len);
+  if (!ws || ws_bytes < need) return fail(GPTQ_ENOWS, "workspace of %zu bytes needed", need);
+  if (!aligned(ws, 256)) return fail(GPTQ_EINVAL, "workspace must be 256-byte aligned");
+  const uint32_t* pq[3] = {qq, qk, qv};
+  const float* ps[3] = {sq, sk, sv};
+  const uint8_t* pz[3] = {zq, zk, zv};
+  hipError_t e = gptq::attn_launch(static_cast<const _Float16*>(X), n_tok, d, ldx, pq, ps, pz,
+                                   bits, group, seq_len, static_cast<_Float16*>(O), ldo, ws,
+                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gptq_attention_forward");
+  return GPTQ_OK;
+}
+
+size_t gptq_residual_linear_workspace_size(int64_t n_tok, int64_t d_in, int64_t d_out) {
+  if (n_tok < 1 || d_in < 32 || d_in % 32 != 0 || d_out < 1 || d_in > (int64_t)1 << 20 ||
+      d_out > (int64_t)1 << 20)
+    return 0;
+  return gptq::residual_ws_bytes(n_tok, d_in, d_out);
+}
+
+int gptq_residual_linear(const void* X, int64_t n_tok, int64_t d_in, int64_t ldx, const void* R,
+                         int64_t ldr, const uint32_t* q, const float* s, const uint8_t* z,
+                         int64_t d_out, int bits, int group, void* Hout, int64_t ldh, void* ws,
+                         size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  int rc;
+  if ((rc = check_layer(GPTQ_F16, d_out, d_in)) != GPTQ_OK) return rc;
+  if ((rc = check_packed(bits, group, d_in)) != GPTQ_OK) return rc;
+  if (n_tok < 0) return fail(GPTQ_EINVAL, "n_tok < 0");
+  if (ldx < d_in || ldr < d_out || ldh < d_out)
+    return fail(GPTQ_EINVAL, "ldx >= d_in, ldr >= d_out and ldh >= d_out required");
+  if (n_tok == 0) return GPTQ_OK;
+  if (!X || !R || !q || !s || !z || !Hout)
+    return fail(GPTQ_EINVAL, "X, R, the packed layer and Hout must not be NULL");
+  const size_t need = gptq::residual_ws_bytes(n_tok, d_in, d_out);
+  if (!ws || ws_bytes < need) return fail(GPTQ_ENOWS, "workspace of %zu bytes needed", need);
+  if (!aligned(ws, 256)) return fail(GPTQ_EINVAL, "workspace must be 256-byte aligned");
+  hipError_t e = gptq::residual_launch(static_cast<const _Float16*>(X), n_tok, d_in, ldx,
+                                       static_cast<const _Float16*>(R), ldr, q, s, z, d_out, bits,
+                                       group, static_cast<_Float16*>(Hout), ldh, ws,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gptq_residual_linear");
+  return GPTQ_OK;
+}
+
 // ---------------------------------------------------------------- instrumentation
 int gptq_profile_enable(int on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);

@@ -108,6 +108,27 @@ hipError_t mlp_launch(const void* X, int64_t n_tok, int64_t d, int64_t ldx,
                       const uint32_t* qg, const float* sg, const uint8_t* zg,
                       const uint32_t* qu, const float* su, const uint8_t* zu, int64_t d_ff,
                       int bits, int group, void* Y, int64_t ldy, void* ws, hipStream_t s);
+// W^ rows of a packed layer into float32 [rows x d]; fp16 token rows into float32 [rows x d].
+void dequant_rows_f32(const uint32_t* q, const float* sc, const uint8_t* z, int64_t rows,
+                      int64_t d, int bits, int64_t g, float* dst, hipStream_t s);
+void f16_rows_to_f32(const _Float16* X, int64_t ldx, int64_t rows, int64_t d, float* dst,
+                     hipStream_t s);
+
+// ---------------------------------------------------------------- attention half (attn.hip)
+constexpr int ATTN_HEAD_DIM = 128;
+hipError_t rmsnorm_launch(const _Float16* x, int64_t ldx, int64_t n_tok, int64_t d,
+                          const _Float16* gamma, double eps, _Float16* y, int64_t ldy,
+                          hipStream_t s);
+size_t attn_ws_bytes(int64_t n_tok, int64_t d, int64_t seq_len);
+hipError_t attn_launch(const _Float16* X, int64_t n_tok, int64_t d, int64_t ldx,
+                       const uint32_t* const pq[3], const float* const ps[3],
+                       const uint8_t* const pz[3], int bits, int group, int64_t seq_len,
+                       _Float16* O, int64_t ldo, void* ws, hipStream_t s);
+size_t residual_ws_bytes(int64_t n_tok, int64_t d_in, int64_t d_out);
+hipError_t residual_launch(const _Float16* X, int64_t n_tok, int64_t d_in, int64_t ldx,
+                           const _Float16* R, int64_t ldr, const uint32_t* q, const float* sc,
+                           const uint8_t* z, int64_t d_out, int bits, int group, _Float16* Hout,
+                           int64_t ldh, void* ws, hipStream_t s);
 
 // ---------------------------------------------------------------- weight-only product (gemv.hip)
 // y[n x d_row] = x[n x d_col] (fp16) * W^T with W^ = s (code - z) read from the packed format.

@@ -69,6 +69,17 @@ unsigned grid_of(int64_t n) {
 
 }  // namespace
 
+void dequant_rows_f32(const uint32_t* q, const float* sc, const uint8_t* z, int64_t rows,
+                      int64_t d, int bits, int64_t g, float* dst, hipStream_t s) {
+  hipLaunchKernelGGL(mlp_dequant, dim3(grid_of(rows * d)), dim3(256), 0, s, q, sc, z, rows, d,
+                     bits, g, dst);
+}
+
+void f16_rows_to_f32(const _Float16* X, int64_t ldx, int64_t rows, int64_t d, float* dst,
+                     hipStream_t s) {
+  hipLaunchKernelGGL(mlp_x_to_f32, dim3(grid_of(rows * d)), dim3(256), 0, s, X, ldx, rows, d, dst);
+}
+
 size_t mlp_ws_bytes(int64_t n_tok, int64_t d, int64_t d_ff) {
   const int64_t t = n_tok < MLP_CHUNK ? n_tok : MLP_CHUNK;
   return align_up((size_t)2 * d_ff * d * sizeof(float), 256) +
@@ -91,10 +102,8 @@ hipError_t mlp_launch(const void* X, int64_t n_tok, int64_t d, int64_t ldx,
   hipError_t e;
   {
     ProfScope ps("mlp_elementwise", s);
-    hipLaunchKernelGGL(mlp_dequant, dim3(grid_of(d_ff * d)), dim3(256), 0, s, qg, sg, zg, d_ff, d,
-                       bits, g, Wcat);
-    hipLaunchKernelGGL(mlp_dequant, dim3(grid_of(d_ff * d)), dim3(256), 0, s, qu, su, zu, d_ff, d,
-                       bits, g, Wcat + d_ff * d);
+    dequant_rows_f32(qg, sg, zg, d_ff, d, bits, g, Wcat, s);
+    dequant_rows_f32(qu, su, zu, d_ff, d, bits, g, Wcat + d_ff * d, s);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const _Float16* Xh = static_cast<const _Float16*>(X);
@@ -103,8 +112,7 @@ hipError_t mlp_launch(const void* X, int64_t n_tok, int64_t d, int64_t ldx,
     const int64_t rows = n_tok - t0 < MLP_CHUNK ? n_tok - t0 : MLP_CHUNK;
     {
       ProfScope ps("mlp_elementwise", s);
-      hipLaunchKernelGGL(mlp_x_to_f32, dim3(grid_of(rows * d)), dim3(256), 0, s, Xh + t0 * ldx,
-                         ldx, rows, d, X32);
+      f16_rows_to_f32(Xh + t0 * ldx, ldx, rows, d, X32, s);
     }
     // A = X32 [rows x d] times Wcat^T (op(B)[k][n] = Wcat[n][k])
     if ((e = gemm_f32({rows, 2 * d_ff, d, X32, d, 0, 0, Wcat, d, 1, 0, A, 2 * d_ff, 0, 1.0f, 0.0f},

@@ -61,6 +61,13 @@ _SIGS = {
     "gptq_mlp_forward_workspace_size": ([_i64, _i64, _i64], _sz),
     "gptq_mlp_forward": ([_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _int,
                           _int, _vp, _i64, _vp, _sz, _vp], _int),
+    "gptq_rmsnorm": ([_vp, _i64, _i64, _i64, _vp, ctypes.c_double, _vp, _i64, _vp], _int),
+    "gptq_attention_forward_workspace_size": ([_i64, _i64, _i64], _sz),
+    "gptq_attention_forward": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _int, _int, _i64, _vp, _i64, _vp, _sz, _vp], _int),
+    "gptq_residual_linear_workspace_size": ([_i64, _i64, _i64], _sz),
+    "gptq_residual_linear": ([_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _int, _int,
+                              _vp, _i64, _vp, _sz, _vp], _int),
     "gptq_profile_enable": ([_int], _int),
     "gptq_profile_only": ([ctypes.c_char_p], _int),
     "gptq_profile_reset": ([], _int),
@@ -276,6 +283,54 @@ def mlp_forward(X, gate, up, bits: int, group: int, Y=None, ws=None, stream=None
                                   bits, group, Y.data_ptr(), Y.stride(0), ws.data_ptr(),
                                   ws.numel() * ws.element_size(), _stream_handle(stream)))
     return Y
+
+
+def rmsnorm(x, gamma, eps: float = 1e-6, y=None, stream=None):
+    """y [n_tok x d] fp16 = x / sqrt(mean(x^2) + eps) * gamma per token (gptq_rmsnorm)."""
+    torch = _torch()
+    n_tok, d = x.shape
+    assert x.stride(1) == 1 and gamma.is_contiguous() and gamma.numel() == d
+    if y is None:
+        y = torch.empty((n_tok, d), dtype=torch.float16, device=x.device)
+    _check(lib().gptq_rmsnorm(x.data_ptr(), n_tok, d, x.stride(0), gamma.data_ptr(), float(eps),
+                              y.data_ptr(), y.stride(0), _stream_handle(stream)))
+    return y
+
+
+def attention_forward(X, q, k, v, bits: int, group: int, seq_len: int, O=None, ws=None,
+                      stream=None):
+    """O [n_tok x d] fp16: causal attention with rotary embedding over sequences of seq_len
+    tokens, on q, k, v = X W^T from the packed q/k/v layers (gptq_attention_forward)."""
+    torch = _torch()
+    n_tok, d = X.shape
+    assert X.stride(1) == 1 and all(p[0].shape[0] == d for p in (q, k, v))
+    if O is None:
+        O = torch.empty((n_tok, d), dtype=torch.float16, device=X.device)
+    ws = _workspace(lib().gptq_attention_forward_workspace_size(max(n_tok, 1), d, seq_len),
+                    X.device, ws)
+    ptrs = [t.data_ptr() for p in (q, k, v) for t in p[:3]]
+    _check(lib().gptq_attention_forward(X.data_ptr(), n_tok, d, X.stride(0), *ptrs, bits, group,
+                                        seq_len, O.data_ptr(), O.stride(0), ws.data_ptr(),
+                                        ws.numel() * ws.element_size(), _stream_handle(stream)))
+    return O
+
+
+def residual_linear(X, R, layer, bits: int, group: int, out=None, ws=None, stream=None):
+    """out [n_tok x d_out] fp16 = R + X W^T for one packed layer (gptq_residual_linear)."""
+    torch = _torch()
+    n_tok, d_in = X.shape
+    d_out = layer[0].shape[0]
+    assert X.stride(1) == 1 and R.stride(1) == 1 and R.shape == (n_tok, d_out)
+    if out is None:
+        out = torch.empty((n_tok, d_out), dtype=torch.float16, device=X.device)
+    ws = _workspace(lib().gptq_residual_linear_workspace_size(max(n_tok, 1), d_in, d_out),
+                    X.device, ws)
+    _check(lib().gptq_residual_linear(X.data_ptr(), n_tok, d_in, X.stride(0), R.data_ptr(),
+                                      R.stride(0), layer[0].data_ptr(), layer[1].data_ptr(),
+                                      layer[2].data_ptr(), d_out, bits, group, out.data_ptr(),
+                                      out.stride(0), ws.data_ptr(),
+                                      ws.numel() * ws.element_size(), _stream_handle(stream)))
+    return out
 
 
 def profile_enable(on=True):

@@ -210,3 +210,55 @@ def test_mlp_forward_validation(lib):
     assert call(X=None) == G.EINVAL
     assert call(wsz=ws - 1) == G.ENOWS
     assert call(n=0) == G.OK
+
+
+def test_attention_half_validation(lib):
+    # rmsnorm: no workspace; shapes, strides, eps and alignment
+    r = lib.gptq_rmsnorm
+
+    def rn(n=10, d=64, ldx=64, ldy=64, eps=1e-6, x=FAKE, y=FAKE, g=FAKE):
+        return r(x, n, d, ldx, g, eps, y, ldy, None)
+
+    assert rn(d=60, ldx=64, ldy=64) == G.EINVAL    # d not a multiple of 8
+    assert rn(ldx=32) == G.EINVAL
+    assert rn(ldy=68) == G.EINVAL                  # not a multiple of 8
+    assert rn(eps=-1.0) == G.EINVAL
+    assert rn(eps=float("nan")) == G.EINVAL
+    assert rn(x=None) == G.EINVAL
+    assert rn(x=ctypes.c_void_p(0x10008)) == G.EINVAL             # not 16-byte aligned
+    assert rn(n=0) == G.OK
+
+    a = lib.gptq_attention_forward
+    ws = lib.gptq_attention_forward_workspace_size(300, 256, 128)
+    assert ws >= 3 * 256 * 256 * 4                 # the dequantized q, k and v weights
+    assert lib.gptq_attention_forward_workspace_size(300, 200, 128) == 0
+    assert lib.gptq_attention_forward_workspace_size(300, 256, 0) == 0
+
+    def at(n=300, d=256, ldx=256, bits=4, group=128, L=128, ldo=256, wsz=ws, O=FAKE):
+        return a(FAKE, n, d, ldx, *([FAKE] * 9), bits, group, L, O, ldo, FAKE, wsz, None)
+
+    assert at(d=192, ldx=192, ldo=192) == G.EINVAL  # not a multiple of the head width
+    assert at(bits=5) == G.EINVAL
+    assert at(group=96) == G.EINVAL
+    assert at(L=0) == G.EINVAL
+    assert at(ldx=128) == G.EINVAL
+    assert at(ldo=260) == G.EINVAL                 # not a multiple of 8
+    assert at(O=None) == G.EINVAL
+    assert at(O=ctypes.c_void_p(0x10002)) == G.EINVAL
+    assert at(wsz=ws - 1) == G.ENOWS
+    assert at(n=0) == G.OK
+
+    rl = lib.gptq_residual_linear
+    ws2 = lib.gptq_residual_linear_workspace_size(100, 256, 128)
+    assert ws2 >= 128 * 256 * 4
+
+    def res(n=100, d_in=256, d_out=128, ldx=256, ldr=128, ldh=128, bits=4, group=128, wsz=ws2):
+        return rl(FAKE, n, d_in, ldx, FAKE, ldr, FAKE, FAKE, FAKE, d_out, bits, group, FAKE, ldh,
+                  FAKE, wsz, None)
+
+    assert res(d_in=100, ldx=100) == G.EINVAL
+    assert res(bits=1) == G.EINVAL
+    assert res(ldr=64) == G.EINVAL
+    assert res(ldh=64) == G.EINVAL
+    assert res(wsz=ws2 - 1) == G.ENOWS
+    assert res(n=0) == G.OK
