@@ -16,7 +16,9 @@ recorded by the library around each launch on the stream it runs on) and the CPU
 on a bounded sample of the same workload.  After the timed steps, outside the metric: the
 weight-only quantized product over packed weights (`w4a16`) and AWQ's activation-aware scale
 search on the same layer and tokens (`awq`), with the layer losses of round-to-nearest, of
-AWQ's choice and of the GPTQ output.
+AWQ's choice and of the GPTQ output; and one LLaMA-7B-shaped decoder layer quantized layer
+by layer on the same tokens (`decoder_block`: each sub-layer calibrated on the output of the
+quantized sub-layers before it, through RMSNorm, rotary causal attention and the MLP).
 """
 
 import argparse
@@ -47,6 +49,8 @@ def parse():
                    help="skip the weight-only quantized product leg")
     p.add_argument("--no-awq", action="store_true",
                    help="skip the AWQ scale-search leg after the timed steps")
+    p.add_argument("--no-block", action="store_true",
+                   help="skip the layer-sequential decoder-block leg after the timed steps")
     p.add_argument("--cpu-tokens", type=int, default=16384)
     p.add_argument("--cpu-rows", type=int, default=128)
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -212,6 +216,68 @@ def awq_leg(G, torch, Wd, Xd, H, gptq_out, spec, n_grid=20):
             "scale_rtn_ms": ms_r,
             "absmean": {"ms": ms_a / n_a, "achieved": am_gbs, "peak": PEAK["hbm"],
                         "unit": "GB/s", "frac": am_gbs / PEAK["hbm"]}}
+
+
+def block_leg(G, torch, Xd, spec, seq_len=2048, d_ff=11008):
+    """Layer-sequential quantization of one LLaMA-7B-shaped decoder layer on the bench's tokens
+    (block.quantize_decoder_block: q/k/v_proj on rmsnorm(x), o_proj on the attention output of
+    the quantized q/k/v, gate/up_proj on rmsnorm of the residual, down_proj on the MLP product
+    of the quantized gate/up), with random fp16 weights ~ N(0, 0.02^2) and norm weights
+    exp(0.2 N(0, 1)).  Wall time from events on the launch stream, the time of each kernel
+    family, and the attention kernel against the fp32 vector peak (2 * 128 * l (l + 1) flops
+    per head and sequence of l tokens: q.k and p.v over the causal pairs) and the forward
+    products against the fp32 MFMA peak."""
+    from post_weight_quantization_24_amd import block as BLK
+    n_tok, d = Xd.shape
+    dev = Xd.device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    shapes = {"q_proj": (d, d), "k_proj": (d, d), "v_proj": (d, d), "o_proj": (d, d),
+              "gate_proj": (d_ff, d), "up_proj": (d_ff, d), "down_proj": (d, d_ff)}
+    W = {k: (torch.randn(s, generator=gen, device=dev) * 0.02).to(torch.float16)
+         for k, s in shapes.items()}
+    g1, g2 = (torch.exp(0.2 * torch.randn(d, generator=gen, device=dev)).to(torch.float16)
+              for _ in range(2))
+    BLK.quantize_decoder_block(W, Xd, g1, g2, spec, seq_len)          # warm-up
+    torch.cuda.synchronize()
+    G.profile_reset()
+    G.profile_only(None)
+    G.profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    r = BLK.quantize_decoder_block(W, Xd, g1, g2, spec, seq_len)
+    e1.record()
+    torch.cuda.synchronize()
+    G.profile_enable(False)
+    ms = e0.elapsed_time(e1)
+    fams = {}
+    for f in ("hessian_mfma", "hessian_reduce", "prep_gemm", "prep_leaf", "prep_damp", "quant_block",
+              "lazy_gemm", "quant_group_params", "quant_convert", "check", "check_gemm",
+              "attention", "block_gemm", "mlp_gemm", "block_elementwise", "mlp_elementwise"):
+        n, t = G.profile_read(f)
+        if n:
+            fams[f] = {"launches": n, "ms": t}
+    n_seq_full, tail = divmod(n_tok, seq_len)
+    pairs = n_seq_full * seq_len * (seq_len + 1) + tail * (tail + 1)
+    attn_flops = 2.0 * 128 * pairs * (d // 128)
+    n_a, ms_a = G.profile_read("attention")
+    attn_tf = attn_flops / (ms_a / 1e3) / 1e12
+    fwd_flops = 2.0 * n_tok * d * (4 * d + 2 * d_ff)
+    ms_f = sum(G.profile_read(f)[1] for f in ("block_gemm", "mlp_gemm"))
+    fwd_tf = fwd_flops / (ms_f / 1e3) / 1e12
+    weights = sum(a * b for a, b in shapes.values())
+    out = {"config": {"d": d, "d_ff": d_ff, "heads": d // 128, "seq_len": seq_len, "n_tok": n_tok,
+                      "bits": spec.bits, "group": spec.group, "sym": bool(spec.sym),
+                      "block": spec.block},
+           "ms": ms, "weights": weights, "weights_per_s": weights / (ms / 1e3),
+           "families_ms": fams,
+           "attention": {"launches": n_a, "ms": ms_a, "achieved": attn_tf, "peak": 157.3,
+                         "unit": "TFLOP/s", "bound": "alu", "frac": attn_tf / 157.3},
+           "forward_gemm": {"ms": ms_f, "achieved": fwd_tf, "peak": PEAK["mfma_f32"],
+                            "unit": "TFLOP/s", "frac": fwd_tf / PEAK["mfma_f32"]},
+           "losses": {k: r["loss_" + k] for k in shapes}}
+    del r, W
+    return out
 
 
 def cpu_baseline(W, X_sample, n_tok_full, spec, rows):
@@ -413,6 +479,11 @@ def main():
     if not a.no_awq:
         awq = awq_leg(G, torch, Wd, Xd, H, (qweight, scales, zeros), spec)
 
+    # ---- one decoder layer quantized layer by layer on the same tokens (7B shapes)
+    blk = None
+    if not a.no_block and d_col == 4096 and Xd.dtype == torch.float16:
+        blk = block_leg(G, torch, Xd, G.Spec.make(4, 128, False, 128, wl.damp))
+
     cpu = None
     if not a.no_cpu:
         cpu = cpu_baseline(W, X_sample, n_tok, spec_d, min(a.cpu_rows, d_row))
@@ -441,6 +512,7 @@ def main():
         "quantize_only": {"value": d_row * d_col / (quant_ms / 1e3), "unit": "weights/s"},
         "w4a16": w4,
         "awq": awq,
+        "decoder_block": blk,
         "input_gen_s": gen_s,
     }
     print(json.dumps(out))
