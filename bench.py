@@ -226,7 +226,8 @@ def block_leg(G, torch, Xd, spec, seq_len=2048, d_ff=11008):
     exp(0.2 N(0, 1)).  Wall time from events on the launch stream, the time of each kernel
     family, and the attention kernel against the fp32 vector peak (2 * 128 * l (l + 1) flops
     per head and sequence of l tokens: q.k and p.v over the causal pairs) and the forward
-    products against the fp32 MFMA peak."""
+    products (fp16 activations times the codes as fp16 integers, 2 n_tok d (4 d + 2 d_ff)
+    flops) against the fp16 MFMA peak."""
     from post_weight_quantization_24_amd import block as BLK
     n_tok, d = Xd.shape
     dev = Xd.device
@@ -273,8 +274,8 @@ def block_leg(G, torch, Xd, spec, seq_len=2048, d_ff=11008):
            "families_ms": fams,
            "attention": {"launches": n_a, "ms": ms_a, "achieved": attn_tf, "peak": 157.3,
                          "unit": "TFLOP/s", "bound": "alu", "frac": attn_tf / 157.3},
-           "forward_gemm": {"ms": ms_f, "achieved": fwd_tf, "peak": PEAK["mfma_f32"],
-                            "unit": "TFLOP/s", "frac": fwd_tf / PEAK["mfma_f32"]},
+           "forward_gemm": {"ms": ms_f, "achieved": fwd_tf, "peak": PEAK["mfma_f16"],
+                            "unit": "TFLOP/s", "frac": fwd_tf / PEAK["mfma_f16"]},
            "losses": {k: r["loss_" + k] for k in shapes}}
     del r, W
     return out

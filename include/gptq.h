@@ -223,13 +223,15 @@ int gptq_awq_search(const void* W, int w_dtype, int64_t d_row, int64_t d_col, co
  *     Y[t][j] = float16( silu(sum_c X[t][c] G^[j][c]) * sum_c X[t][c] U^[j][c] ),
  *     silu(a) = a / (1 + exp(-a)),
  * with G^ and U^ dequantized from the packed gate_proj and up_proj as gptq_quantize_layer
- * writes them (both [d_ff x d], the same bits and group).  Products in float32 on the
- * matrix cores, tokens in chunks of 8192.
- *   X    [n_tok x d] fp16 (x_dtype GPTQ_F16), row stride ldx >= d.
+ * writes them (both [d_ff x d], the same bits and group).  Products group by group on the
+ * fp16 matrix cores (fp16 X times the exact integers code - z, fp32 sums scaled by s),
+ * tokens in chunks of 8192.
+ *   X    [n_tok x d] fp16 (x_dtype GPTQ_F16), row stride ldx >= d, a multiple of 8; X
+ *        16-byte aligned.
  *   Y    [n_tok x d_ff] fp16 output, row stride ldy >= d_ff.
  *   d a multiple of 32; bits 2, 3, 4 or 8; group 0 or a multiple of 16 dividing d.
  *   Workspace: gptq_mlp_forward_workspace_size(n_tok, d, d_ff) bytes, 256-byte aligned
- *   (the dequantized weights and one chunk's float32 input and products).
+ *   (the codes expanded to fp16 integers and one chunk's float32 products).
  * Errors: GPTQ_EINVAL, GPTQ_ENOWS, GPTQ_EHIP. */
 size_t gptq_mlp_forward_workspace_size(int64_t n_tok, int64_t d, int64_t d_ff);
 int gptq_mlp_forward(const void* X, int x_dtype, int64_t n_tok, int64_t d, int64_t ldx,
@@ -252,21 +254,22 @@ int gptq_mlp_forward(const void* X, int x_dtype, int64_t n_tok, int64_t d, int64
  *
  * gptq_attention_forward: O = float16( attention(rope(q), rope(k), v) ) with
  *   q, k, v = float16(X W^T) for the packed q_proj, k_proj and v_proj (each [d x d], the
- *   same bits and group, in gptq_quantize_layer's format; products in float32 on the matrix
- *   cores).  Causal multi-head self-attention, heads of 128 channels (head h is channels
+ *   same bits and group, in gptq_quantize_layer's format; products group by group on the
+ *   fp16 matrix cores as for gptq_mlp_forward).  Causal multi-head self-attention, heads of 128 channels (head h is channels
  *   [128 h, 128 h + 128)), softmax of q.k / sqrt(128) over the keys at or before the query.
  *   Rotary embedding: channels i and i + 64 of a head turn by pos * 10000^(-2i/128), angles
  *   in float64.  The tokens form independent sequences [0, seq_len), [seq_len, 2 seq_len),
  *   ...; pos counts from 0 in each; the last one may be shorter.
- *   X  [n_tok x d] fp16, row stride ldx >= d;  O [n_tok x d] fp16, ldo >= d, ldo a multiple
- *   of 8 and O 16-byte aligned.  d a multiple of 128; bits 2, 3, 4 or 8; group 0 or a
+ *   X  [n_tok x d] fp16, row stride ldx >= d;  O [n_tok x d] fp16, ldo >= d; ldx and ldo
+ *   multiples of 8, X and O 16-byte aligned.  d a multiple of 128; bits 2, 3, 4 or 8; group 0 or a
  *   multiple of 16 dividing d; 1 <= seq_len <= 2^20.
  *   Workspace: gptq_attention_forward_workspace_size(n_tok, d, seq_len) bytes, 256-byte
- *   aligned (the dequantized weights, one chunk of whole sequences in float32, the angles).
+ *   aligned (the codes as fp16 integers, one chunk of whole sequences in float32, the angles).
  *
  * gptq_residual_linear: Hout = float16( R + X W^T ) for one packed layer W [d_out x d_in]
  *   (o_proj: X the attention output, R the block input).
- *   X [n_tok x d_in] fp16, ldx >= d_in; R and Hout [n_tok x d_out] fp16, ldr, ldh >= d_out.
+ *   X [n_tok x d_in] fp16, ldx >= d_in a multiple of 8, X 16-byte aligned; R and Hout
+ *   [n_tok x d_out] fp16, ldr, ldh >= d_out.
  *   d_in a multiple of 32; bits and group as above (group divides d_in).
  *   Workspace: gptq_residual_linear_workspace_size(n_tok, d_in, d_out) bytes, 256-byte aligned.
  *

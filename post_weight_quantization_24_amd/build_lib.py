@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgptq.so")
 SOURCES = ["api.hip", "hessian.hip", "gemm.hip", "prep.hip", "quant.hip", "check.hip", "gemv.hip",
-           "awq.hip", "mlp.hip", "attn.hip"]
+           "awq.hip", "mlp.hip", "attn.hip", "qgemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -380,8 +380,10 @@ int gptq_mlp_forward(const void* X, int x_dtype, int64_t n_tok, int64_t d, int64
   if (n_tok < 0) return fail(GPTQ_EINVAL, "n_tok < 0");
   if (n_tok == 0) return GPTQ_OK;
   if (ldx < d || ldy < d_ff) return fail(GPTQ_EINVAL, "ldx >= d and ldy >= d_ff required");
+  if (ldx % 8 != 0) return fail(GPTQ_EINVAL, "ldx must be a multiple of 8");
   if (!X || !qgate || !sgate || !zgate || !qup || !sup || !zup || !Y)
     return fail(GPTQ_EINVAL, "X, the packed gate and up layers and Y must not be NULL");
+  if (!aligned(X, 16)) return fail(GPTQ_EINVAL, "X must be 16-byte aligned");
   const size_t need = gptq::mlp_ws_bytes(n_tok, d, d_ff);
   if (!ws || ws_bytes < need) return fail(GPTQ_ENOWS, "workspace of %zu bytes needed", need);
   if (!aligned(ws, 256)) return fail(GPTQ_EINVAL, "workspace must be 256-byte aligned");
@@ -442,12 +444,12 @@ int gptq_attention_forward(const void* X, int64_t n_tok, int64_t d, int64_t ldx,
   if ((rc = check_packed(bits, group, d)) != GPTQ_OK) return rc;
   if (seq_len < 1 || seq_len > (int64_t)1 << 20) return fail(GPTQ_EINVAL, "seq_len out of range");
   if (n_tok < 0) return fail(GPTQ_EINVAL, "n_tok < 0");
-  if (ldx < d || ldo < d || ldo % 8 != 0)
-    return fail(GPTQ_EINVAL, "ldx >= d, ldo >= d and ldo a multiple of 8 required");
+  if (ldx < d || ldo < d || ldo % 8 != 0 || ldx % 8 != 0)
+    return fail(GPTQ_EINVAL, "ldx >= d, ldo >= d and both multiples of 8 required");
   if (n_tok == 0) return GPTQ_OK;
   if (!X || !qq || !sq || !zq || !qk || !sk || !zk || !qv || !sv || !zv || !O)
     return fail(GPTQ_EINVAL, "X, the packed q/k/v layers and O must not be NULL");
-  if (!aligned(O, 16)) return fail(GPTQ_EINVAL, "O must be 16-byte aligned");
+  if (!aligned(O, 16) || !aligned(X, 16)) return fail(GPTQ_EINVAL, "X and O must be 16-byte aligned");
   const size_t need = gptq::attn_ws_bytes(n_tok, d, seq_len);
   if (!ws || ws_bytes < need) return fail(GPTQ_ENOWS, "workspace of %zu bytes needed", need);
   if (!aligned(ws, 256)) return fail(GPTQ_EINVAL, "workspace must be 256-byte aligned");
@@ -477,11 +479,12 @@ int gptq_residual_linear(const void* X, int64_t n_tok, int64_t d_in, int64_t ldx
   if ((rc = check_layer(GPTQ_F16, d_out, d_in)) != GPTQ_OK) return rc;
   if ((rc = check_packed(bits, group, d_in)) != GPTQ_OK) return rc;
   if (n_tok < 0) return fail(GPTQ_EINVAL, "n_tok < 0");
-  if (ldx < d_in || ldr < d_out || ldh < d_out)
-    return fail(GPTQ_EINVAL, "ldx >= d_in, ldr >= d_out and ldh >= d_out required");
+  if (ldx < d_in || ldr < d_out || ldh < d_out || ldx % 8 != 0)
+    return fail(GPTQ_EINVAL, "ldx >= d_in (a multiple of 8), ldr >= d_out and ldh >= d_out required");
   if (n_tok == 0) return GPTQ_OK;
   if (!X || !R || !q || !s || !z || !Hout)
     return fail(GPTQ_EINVAL, "X, R, the packed layer and Hout must not be NULL");
+  if (!aligned(X, 16)) return fail(GPTQ_EINVAL, "X must be 16-byte aligned");
   const size_t need = gptq::residual_ws_bytes(n_tok, d_in, d_out);
   if (!ws || ws_bytes < need) return fail(GPTQ_ENOWS, "workspace of %zu bytes needed", need);
   if (!aligned(ws, 256)) return fail(GPTQ_EINVAL, "workspace must be 256-byte aligned");

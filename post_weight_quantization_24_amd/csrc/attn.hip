@@ -8,9 +8,10 @@
 // pairs (i, i + 64) with theta = 10000, and positions that restart at every sequence of
 // seq_len tokens (tokens [0, seq_len), [seq_len, 2 seq_len), ... form the sequences).
 //
-// Every tensor a quantized sub-layer reads is stored in float16; the products run on the fp32
-// MFMA GEMM over weights dequantized once to float32, the rotary angles and the norm are
-// formed in float64, the attention itself in float32 with a running softmax.
+// Every tensor a quantized sub-layer reads is stored in float16; the products run group by
+// group on the fp16 matrix cores over the codes expanded to fp16 integers (qgemm.hip), the
+// rotary angles and the norm are formed in float64, the attention itself in float32 with a
+// running softmax.
 
 #include <cmath>
 
@@ -275,8 +276,7 @@ hipError_t rmsnorm_launch(const _Float16* x, int64_t ldx, int64_t n_tok, int64_t
 size_t attn_ws_bytes(int64_t n_tok, int64_t d, int64_t seq_len) {
   const int64_t t = chunk_tokens(n_tok, seq_len);
   const int64_t L = seq_len < n_tok ? seq_len : n_tok;
-  return align_up((size_t)3 * d * d * sizeof(float), 256) +
-         align_up((size_t)t * d * sizeof(float), 256) +
+  return align_up((size_t)3 * d * d * sizeof(_Float16), 256) +
          align_up((size_t)t * 3 * d * sizeof(float), 256) +
          align_up((size_t)L * (HD / 2) * sizeof(double2), 256);
 }
@@ -289,29 +289,25 @@ hipError_t attn_launch(const _Float16* X, int64_t n_tok, int64_t d, int64_t ldx,
   const int64_t T = chunk_tokens(n_tok, seq_len);
   const int64_t L = seq_len < n_tok ? seq_len : n_tok;
   char* p = static_cast<char*>(ws);
-  float* Wcat = reinterpret_cast<float*>(p);
-  p += align_up((size_t)3 * d * d * sizeof(float), 256);
-  float* X32 = reinterpret_cast<float*>(p);
-  p += align_up((size_t)T * d * sizeof(float), 256);
+  _Float16* Bint = reinterpret_cast<_Float16*>(p);
+  p += align_up((size_t)3 * d * d * sizeof(_Float16), 256);
   float* A = reinterpret_cast<float*>(p);
   p += align_up((size_t)T * 3 * d * sizeof(float), 256);
   double2* tab = reinterpret_cast<double2*>(p);
   {
     ProfScope ps_("block_elementwise", s);
-    for (int m = 0; m < 3; ++m) dequant_rows_f32(pq[m], ps[m], pz[m], d, d, bits, g, Wcat + m * d * d, s);
+    for (int m = 0; m < 3; ++m) expand_codes_f16(pq[m], pz[m], d, d, bits, g, Bint + m * d * d, s);
     hipLaunchKernelGGL(rope_table, dim3((unsigned)ceil_div(L * (HD / 2), 256)), dim3(256), 0, s, tab, L);
   }
   hipError_t e;
   if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int64_t t0 = 0; t0 < n_tok; t0 += T) {
     const int64_t rows = n_tok - t0 < T ? n_tok - t0 : T;
-    {
-      ProfScope ps_("block_elementwise", s);
-      f16_rows_to_f32(X + t0 * ldx, ldx, rows, d, X32, s);
-    }
-    if ((e = gemm_f32({rows, 3 * d, d, X32, d, 0, 0, Wcat, d, 1, 0, A, 3 * d, 0, 1.0f, 0.0f}, s,
-                      "block_gemm")) != hipSuccess)
-      return e;
+    // A[:, m d : (m + 1) d] = X W_m^T for q, k, v
+    for (int m = 0; m < 3; ++m)
+      if ((e = qgemm_f16(X + t0 * ldx, ldx, rows, Bint + m * d * d, d, d, ps[m], g, A + m * d, 3 * d,
+                         s, "block_gemm")) != hipSuccess)
+        return e;
     {
       ProfScope ps_("block_elementwise", s);
       hipLaunchKernelGGL(qkv_rope, dim3(grid_of(rows * d / 2)), dim3(256), 0, s, A, rows, d, L, tab);
@@ -330,8 +326,7 @@ hipError_t attn_launch(const _Float16* X, int64_t n_tok, int64_t d, int64_t ldx,
 
 size_t residual_ws_bytes(int64_t n_tok, int64_t d_in, int64_t d_out) {
   const int64_t t = n_tok < TOK_CHUNK ? n_tok : TOK_CHUNK;
-  return align_up((size_t)d_out * d_in * sizeof(float), 256) +
-         align_up((size_t)t * d_in * sizeof(float), 256) +
+  return align_up((size_t)d_out * d_in * sizeof(_Float16), 256) +
          align_up((size_t)t * d_out * sizeof(float), 256);
 }
 
@@ -342,25 +337,19 @@ hipError_t residual_launch(const _Float16* X, int64_t n_tok, int64_t d_in, int64
   const int64_t g = group == 0 ? d_in : group;
   const int64_t T = n_tok < TOK_CHUNK ? n_tok : TOK_CHUNK;
   char* p = static_cast<char*>(ws);
-  float* W = reinterpret_cast<float*>(p);
-  p += align_up((size_t)d_out * d_in * sizeof(float), 256);
-  float* X32 = reinterpret_cast<float*>(p);
-  p += align_up((size_t)T * d_in * sizeof(float), 256);
+  _Float16* Bint = reinterpret_cast<_Float16*>(p);
+  p += align_up((size_t)d_out * d_in * sizeof(_Float16), 256);
   float* A = reinterpret_cast<float*>(p);
   {
     ProfScope ps_("block_elementwise", s);
-    dequant_rows_f32(q, sc, z, d_out, d_in, bits, g, W, s);
+    expand_codes_f16(q, z, d_out, d_in, bits, g, Bint, s);
   }
   hipError_t e;
   if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int64_t t0 = 0; t0 < n_tok; t0 += T) {
     const int64_t rows = n_tok - t0 < T ? n_tok - t0 : T;
-    {
-      ProfScope ps_("block_elementwise", s);
-      f16_rows_to_f32(X + t0 * ldx, ldx, rows, d_in, X32, s);
-    }
-    if ((e = gemm_f32({rows, d_out, d_in, X32, d_in, 0, 0, W, d_in, 1, 0, A, d_out, 0, 1.0f, 0.0f}, s,
-                      "block_gemm")) != hipSuccess)
+    if ((e = qgemm_f16(X + t0 * ldx, ldx, rows, Bint, d_out, d_in, sc, g, A, d_out, s,
+                       "block_gemm")) != hipSuccess)
       return e;
     {
       ProfScope ps_("block_elementwise", s);

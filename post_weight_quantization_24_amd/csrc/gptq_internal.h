@@ -108,11 +108,15 @@ hipError_t mlp_launch(const void* X, int64_t n_tok, int64_t d, int64_t ldx,
                       const uint32_t* qg, const float* sg, const uint8_t* zg,
                       const uint32_t* qu, const float* su, const uint8_t* zu, int64_t d_ff,
                       int bits, int group, void* Y, int64_t ldy, void* ws, hipStream_t s);
-// W^ rows of a packed layer into float32 [rows x d]; fp16 token rows into float32 [rows x d].
-void dequant_rows_f32(const uint32_t* q, const float* sc, const uint8_t* z, int64_t rows,
-                      int64_t d, int bits, int64_t g, float* dst, hipStream_t s);
-void f16_rows_to_f32(const _Float16* X, int64_t ldx, int64_t rows, int64_t d, float* dst,
-                     hipStream_t s);
+
+// ---------------------------------------------------------------- packed-layer product (qgemm.hip)
+// B[n][k] = code - z as fp16 for a packed layer [N x K]; C = A W^T group by group on the fp16
+// matrix cores (A fp16 [M x K], rows 16-byte aligned; S the scales [N x K/g]; C fp32).
+void expand_codes_f16(const uint32_t* q, const uint8_t* z, int64_t N, int64_t K, int bits,
+                      int64_t g, _Float16* B, hipStream_t s);
+hipError_t qgemm_f16(const _Float16* A, int64_t lda, int64_t M, const _Float16* B, int64_t N,
+                     int64_t K, const float* S, int64_t g, float* C, int64_t ldc, hipStream_t s,
+                     const char* prof_name);
 
 // ---------------------------------------------------------------- attention half (attn.hip)
 constexpr int ATTN_HEAD_DIM = 128;

@@ -1,0 +1,183 @@
+// Product of fp16 activations with a packed layer on the fp16 matrix cores, group by group:
+//     C[m][n] = sum_g s[n][g] * sum_{k in group g} A[m][k] * (code[n][k] - z[n][g])
+// which is A W^T for the dequantized weights W^ = s (code - z) (page "量化", section GPTQ:
+// the quantized layer's output; the format is the one the column solve writes).
+//
+// The integers code - z (|.| <= 255) are exact in fp16, and so is every product of one with
+// an fp16 activation in the fp32 accumulator, so each group's sum rounds only in its fp32
+// accumulation; the group sums are then scaled and added in fp32.  The codes are expanded
+// once per call into an fp16 matrix [N x K] (code - z), which the tiles read like a plain
+// fp16 operand.
+//
+// Requirements (checked by the callers): K a multiple of 32, g a multiple of 16 dividing K,
+// A's rows 16-byte aligned (lda a multiple of 8).
+//
+// Tiles of 128 x 128 outputs per workgroup of four waves (2 x 2, 64 x 64 per wave: four
+// 32 x 32 MFMA tiles), 64-wide K stages through LDS in two buffers (the next stage is loaded
+// into registers while the current one is multiplied).  Rows of a stage are padded to 72
+// halfs so the eight lanes that a 16-byte LDS read serves at once fall in distinct banks.
+
+#include "gptq_internal.h"
+
+namespace gptq {
+
+namespace {
+
+constexpr int QM = 128, QN = 128, QK = 64;
+constexpr int LDR = QK + 8;                     // halfs per LDS row
+constexpr int STAGE = QM * LDR;                 // halfs per operand stage
+
+__global__ void __launch_bounds__(256)
+expand_codes(const uint32_t* __restrict__ qweight, const uint8_t* __restrict__ zeros, int64_t N,
+             int64_t K, int bits, int64_t g, _Float16* __restrict__ B) {
+  const int64_t n = N * K;
+  const int64_t words_per_row = K * bits / 32;
+  const int64_t n_groups = K / g;
+  const uint32_t mask = (1u << bits) - 1u;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / K, c = i % K;
+    const int64_t bit = c * bits;
+    const uint32_t* wr = qweight + r * words_per_row;
+    uint64_t two = wr[bit / 32];
+    if ((bit % 32) + bits > 32) two |= (uint64_t)wr[bit / 32 + 1] << 32;
+    const int code = (int)((uint32_t)(two >> (bit % 32)) & mask);
+    B[i] = (_Float16)(float)(code - (int)zeros[r * n_groups + c / g]);
+  }
+}
+
+__global__ void __launch_bounds__(256, 2)
+qgemm_k(const _Float16* __restrict__ A, int64_t lda, int64_t M, const _Float16* __restrict__ B,
+        int64_t N, int64_t K, const float* __restrict__ S, int64_t n_groups, int gsteps,
+        float* __restrict__ C, int64_t ldc) {
+  __shared__ _Float16 As[2 * STAGE];
+  __shared__ _Float16 Bs[2 * STAGE];
+  const int64_t tiles_m = (M + QM - 1) / QM;
+  const int64_t tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+  const int64_t m0 = tm * QM, n0 = tn * QN;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w & 1, wn = w >> 1;
+  const int li = lane & 31, lh = lane >> 5;
+
+  // one stage of one operand: 128 rows x 64 halfs = 1024 16-byte pieces, 4 per thread
+  half8 ra[4], rb[4];
+  auto load = [&](int64_t k0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int id = e * 256 + tid;
+      const int row = id >> 3, kc = (id & 7) * 8;
+      const half8 zero = {};
+      const bool kin = k0 + kc < K;
+      ra[e] = m0 + row < M && kin ? *reinterpret_cast<const half8*>(A + (m0 + row) * lda + k0 + kc) : zero;
+      rb[e] = n0 + row < N && kin ? *reinterpret_cast<const half8*>(B + (n0 + row) * K + k0 + kc) : zero;
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int id = e * 256 + tid;
+      const int row = id >> 3, kc = (id & 7) * 8;
+      *reinterpret_cast<half8*>(As + buf * STAGE + row * LDR + kc) = ra[e];
+      *reinterpret_cast<half8*>(Bs + buf * STAGE + row * LDR + kc) = rb[e];
+    }
+  };
+
+  floatx16 acc[2][2], part[2][2];
+  const floatx16 zero16 = {};
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = zero16;
+
+  // the scale of this lane's output column in each of its two N tiles, group grp
+  const int64_t col0 = n0 + wn * 64 + li, col1 = col0 + 32;
+  const float* s0 = S + (col0 < N ? col0 : N - 1) * n_groups;
+  const float* s1 = S + (col1 < N ? col1 : N - 1) * n_groups;
+
+  const int64_t nst = (K + QK - 1) / QK;     // K is a multiple of 32: the last stage may be half
+  load(0);
+  store(0);
+  __syncthreads();
+  int step = 0;
+  int64_t grp = 0;
+  for (int64_t st = 0; st < nst; ++st) {
+    const int buf = (int)(st & 1);
+    if (st + 1 < nst) load((st + 1) * QK);
+    const _Float16* as = As + buf * STAGE;
+    const _Float16* bs = Bs + buf * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < QK / 16; ++kk) {
+      if (st * QK + kk * 16 >= K) break;
+      half8 af[2], bf[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+        af[a] = *reinterpret_cast<const half8*>(as + (wm * 64 + a * 32 + li) * LDR + kk * 16 + lh * 8);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        bf[b] = *reinterpret_cast<const half8*>(bs + (wn * 64 + b * 32 + li) * LDR + kk * 16 + lh * 8);
+      if (step == 0) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+            part[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], zero16, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+            part[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], part[a][b], 0, 0, 0);
+      }
+      if (++step == gsteps) {            // the group ends here: scale its sums into acc
+        step = 0;
+        const float sc0 = s0[grp], sc1 = s1[grp];
+        ++grp;
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int c = 0; c < 16; ++c) {
+            acc[a][0][c] += sc0 * part[a][0][c];
+            acc[a][1][c] += sc1 * part[a][1][c];
+          }
+      }
+    }
+    if (st + 1 < nst) {
+      store(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t col = n0 + wn * 64 + b * 32 + li;
+      if (col >= N) continue;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const int64_t row = m0 + wm * 64 + a * 32 + 8 * (c >> 2) + 4 * lh + (c & 3);
+        if (row < M) C[row * ldc + col] = acc[a][b][c];
+      }
+    }
+}
+
+}  // namespace
+
+void expand_codes_f16(const uint32_t* q, const uint8_t* z, int64_t N, int64_t K, int bits,
+                      int64_t g, _Float16* B, hipStream_t s) {
+  const int64_t blocks = ceil_div(N * K, 256);
+  hipLaunchKernelGGL(expand_codes, dim3((unsigned)(blocks < 16384 ? blocks : 16384)), dim3(256), 0,
+                     s, q, z, N, K, bits, g, B);
+}
+
+hipError_t qgemm_f16(const _Float16* A, int64_t lda, int64_t M, const _Float16* B, int64_t N,
+                     int64_t K, const float* S, int64_t g, float* C, int64_t ldc, hipStream_t s,
+                     const char* prof_name) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  ProfScope ps(prof_name, s);
+  const int64_t tiles = ceil_div(M, QM) * ceil_div(N, QN);
+  hipLaunchKernelGGL(qgemm_k, dim3((unsigned)tiles), dim3(256), 0, s, A, lda, M, B, N, K, S, K / g,
+                     (int)(g / 16), C, ldc);
+  return hipGetLastError();
+}
+
+}  // namespace gptq

@@ -193,7 +193,7 @@ def test_awq_validation(lib):
 def test_mlp_forward_validation(lib):
     f = lib.gptq_mlp_forward
     ws = lib.gptq_mlp_forward_workspace_size(100, 256, 512)
-    assert ws >= 2 * 512 * 256 * 4                  # the dequantized gate and up weights
+    assert ws >= 2 * 512 * 256 * 2                  # the gate and up codes as fp16 integers
     assert lib.gptq_mlp_forward_workspace_size(0, 256, 512) == 0
 
     def call(n=100, d=256, d_ff=512, bits=4, group=128, xdt=0, ldx=256, ldy=512, wsz=ws, X=FAKE):
@@ -207,6 +207,8 @@ def test_mlp_forward_validation(lib):
     assert call(xdt=1) == G.EINVAL                 # X must be fp16
     assert call(ldx=128) == G.EINVAL
     assert call(ldy=256) == G.EINVAL
+    assert call(ldx=260) == G.EINVAL              # not a multiple of 8
+    assert call(X=ctypes.c_void_p(0x10008)) == G.EINVAL   # not 16-byte aligned
     assert call(X=None) == G.EINVAL
     assert call(wsz=ws - 1) == G.ENOWS
     assert call(n=0) == G.OK
@@ -230,7 +232,7 @@ def test_attention_half_validation(lib):
 
     a = lib.gptq_attention_forward
     ws = lib.gptq_attention_forward_workspace_size(300, 256, 128)
-    assert ws >= 3 * 256 * 256 * 4                 # the dequantized q, k and v weights
+    assert ws >= 3 * 256 * 256 * 2                 # the q, k and v codes as fp16 integers
     assert lib.gptq_attention_forward_workspace_size(300, 200, 128) == 0
     assert lib.gptq_attention_forward_workspace_size(300, 256, 0) == 0
 
@@ -243,6 +245,7 @@ def test_attention_half_validation(lib):
     assert at(L=0) == G.EINVAL
     assert at(ldx=128) == G.EINVAL
     assert at(ldo=260) == G.EINVAL                 # not a multiple of 8
+    assert at(ldx=260) == G.EINVAL
     assert at(O=None) == G.EINVAL
     assert at(O=ctypes.c_void_p(0x10002)) == G.EINVAL
     assert at(wsz=ws - 1) == G.ENOWS
@@ -250,7 +253,7 @@ def test_attention_half_validation(lib):
 
     rl = lib.gptq_residual_linear
     ws2 = lib.gptq_residual_linear_workspace_size(100, 256, 128)
-    assert ws2 >= 128 * 256 * 4
+    assert ws2 >= 128 * 256 * 2
 
     def res(n=100, d_in=256, d_out=128, ldx=256, ldr=128, ldh=128, bits=4, group=128, wsz=ws2):
         return rl(FAKE, n, d_in, ldx, FAKE, ldr, FAKE, FAKE, FAKE, d_out, bits, group, FAKE, ldh,
@@ -259,6 +262,7 @@ def test_attention_half_validation(lib):
     assert res(d_in=100, ldx=100) == G.EINVAL
     assert res(bits=1) == G.EINVAL
     assert res(ldr=64) == G.EINVAL
+    assert res(ldx=260) == G.EINVAL
     assert res(ldh=64) == G.EINVAL
     assert res(wsz=ws2 - 1) == G.ENOWS
     assert res(n=0) == G.OK
