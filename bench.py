@@ -457,7 +457,6 @@ def main():
                   ("gate_proj 28672x8192 INT4 g128 (random codes)", bq, bs, bz, 4, 128)]
         own_ok = wl.group % 32 == 0 and d_col <= 32768      # the call's shape limits
         w4 = w4a16_leg(G, torch, dev, layers if own_ok else layers[1:])
-        del bq, bs, bz
         # context: the same product with fp16 weights through the library GEMM (torch), the
         # unquantized alternative whose 4x larger weight read the packed format avoids
         w16 = torch.randn((big_rows, big_cols), device=dev).to(torch.float16)
@@ -473,7 +472,38 @@ def main():
         ref_us = e0.elapsed_time(e1) / 50 * 1e3
         w4[-1]["fp16_library_us"] = ref_us
         w4[-1]["speedup_vs_fp16"] = ref_us / w4[-1]["avg_launch_us"]
-        del w16, xb
+        # the batched regime: 2048 activation rows through the matrix-core path
+        # (gptq_dequant_matmul), against the library fp16 GEMM on the dense weights
+        nb = 2048
+        xm = torch.randn((nb, big_cols), device=dev).to(torch.float16)
+        ym = torch.empty((nb, big_rows), dtype=torch.float32, device=dev)
+        wsm = torch.empty(G.lib().gptq_dequant_matmul_workspace_size(big_rows, big_cols),
+                          dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            G.dequant_matmul(bq, bs, bz, xm, 4, 128, big_cols, y=ym, ws=wsm)
+        torch.cuda.synchronize()
+        G.profile_reset()
+        G.profile_enable(True)
+        for _ in range(10):
+            G.dequant_matmul(bq, bs, bz, xm, 4, 128, big_cols, y=ym, ws=wsm)
+        torch.cuda.synchronize()
+        G.profile_enable(False)
+        n_m, ms_m = G.profile_read("dequant_matmul")
+        n_e, ms_e = G.profile_read("dequant_expand")
+        flops = 2.0 * nb * big_rows * big_cols
+        for _ in range(3):
+            torch.matmul(xm, w16.t())
+        e0.record()
+        for _ in range(10):
+            torch.matmul(xm, w16.t())
+        e1.record()
+        torch.cuda.synchronize()
+        lib_ms = e0.elapsed_time(e1) / 10
+        tf = flops / (ms_m / n_m / 1e3) / 1e12
+        w4[-1]["batched"] = {"n": nb, "product_ms": ms_m / n_m, "expand_ms": ms_e / n_e,
+                             "achieved": tf, "peak": PEAK["mfma_f16"], "unit": "TFLOP/s",
+                             "frac": tf / PEAK["mfma_f16"], "fp16_library_ms": lib_ms}
+        del w16, xb, xm, ym, wsm, bq, bs, bz
 
     # ---- AWQ's activation-aware scale search on the same layer, tokens and H
     awq = None

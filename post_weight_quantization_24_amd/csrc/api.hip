@@ -103,6 +103,15 @@ int check_layer(int w_dtype, int64_t d_row, int64_t d_col) {
   return GPTQ_OK;
 }
 
+int check_packed(int bits, int group, int64_t d) {
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
+    return fail(GPTQ_EINVAL, "bits must be 2, 3, 4 or 8 (got %d)", bits);
+  if (group < 0 || (group > 0 && (group % 16 != 0 || d % group != 0)))
+    return fail(GPTQ_EINVAL, "group must be 0 or a multiple of 16 dividing %lld (got %d)",
+                (long long)d, group);
+  return GPTQ_OK;
+}
+
 }  // namespace
 
 namespace gptq {
@@ -295,6 +304,45 @@ int gptq_dequant_matvec(const uint32_t* qweight, const float* scales, const uint
   return GPTQ_OK;
 }
 
+size_t gptq_dequant_matmul_workspace_size(int64_t d_row, int64_t d_col) {
+  if (d_row < 1 || d_col < 32 || d_col % 32 != 0 || d_row > (int64_t)1 << 30 || d_col > (int64_t)1 << 20)
+    return 0;
+  return gptq::align_up((size_t)d_row * d_col * sizeof(_Float16), 256);
+}
+
+int gptq_dequant_matmul(const uint32_t* qweight, const float* scales, const uint8_t* zeros,
+                        int64_t d_row, int64_t d_col, int bits, int group, const void* x, int64_t n,
+                        int64_t ldx, float* y, int64_t ldy, void* ws, size_t ws_bytes,
+                        void* stream) {
+  g_last_error.clear();
+  int rc;
+  if ((rc = check_layer(GPTQ_F16, d_row, d_col)) != GPTQ_OK) return rc;
+  if ((rc = check_packed(bits, group, d_col)) != GPTQ_OK) return rc;
+  if (n < 0) return fail(GPTQ_EINVAL, "n < 0");
+  if (ldx < d_col || ldx % 8 != 0 || ldy < d_row)
+    return fail(GPTQ_EINVAL, "ldx >= d_col (a multiple of 8) and ldy >= d_row required");
+  if (n == 0) return GPTQ_OK;
+  if (!qweight || !scales || !zeros || !x || !y)
+    return fail(GPTQ_EINVAL, "qweight, scales, zeros, x and y must not be NULL");
+  if (!aligned(x, 16)) return fail(GPTQ_EINVAL, "x must be 16-byte aligned");
+  const size_t need = gptq_dequant_matmul_workspace_size(d_row, d_col);
+  if (!ws || ws_bytes < need) return fail(GPTQ_ENOWS, "workspace of %zu bytes needed", need);
+  if (!aligned(ws, 256)) return fail(GPTQ_EINVAL, "workspace must be 256-byte aligned");
+  const int64_t g = group == 0 ? d_col : group;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  _Float16* B = static_cast<_Float16*>(ws);
+  {
+    gptq::ProfScope ps("dequant_expand", s);
+    gptq::expand_codes_f16(qweight, zeros, d_row, d_col, bits, g, B, s);
+  }
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess)
+    e = gptq::qgemm_f16(static_cast<const _Float16*>(x), ldx, n, B, d_row, d_col, scales, g, y,
+                        ldy, s, "dequant_matmul");
+  if (e != hipSuccess) return hip_fail(e, "gptq_dequant_matmul");
+  return GPTQ_OK;
+}
+
 // ---------------------------------------------------------------- AWQ scale search
 size_t gptq_act_absmean_workspace_size(int64_t d, int64_t n_tok) {
   if (d < 1 || d > (int64_t)1 << 20 || n_tok < 0) return 0;
@@ -393,14 +441,6 @@ int gptq_mlp_forward(const void* X, int x_dtype, int64_t n_tok, int64_t d, int64
   return GPTQ_OK;
 }
 
-static int check_packed(int bits, int group, int64_t d) {
-  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
-    return fail(GPTQ_EINVAL, "bits must be 2, 3, 4 or 8 (got %d)", bits);
-  if (group < 0 || (group > 0 && (group % 16 != 0 || d % group != 0)))
-    return fail(GPTQ_EINVAL, "group must be 0 or a multiple of 16 dividing %lld (got %d)",
-                (long long)d, group);
-  return GPTQ_OK;
-}
 
 int gptq_rmsnorm(const void* x, int64_t n_tok, int64_t d, int64_t ldx, const void* gamma,
                  double eps, void* y, int64_t ldy, void* stream) {

@@ -53,6 +53,9 @@ _SIGS = {
                             _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "gptq_dequant_matvec": ([_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _int, _i64, _i64, _vp,
                              _i64, _vp], _int),
+    "gptq_dequant_matmul_workspace_size": ([_i64, _i64], _sz),
+    "gptq_dequant_matmul": ([_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64,
+                             _vp, _sz, _vp], _int),
     "gptq_act_absmean_workspace_size": ([_i64, _i64], _sz),
     "gptq_act_absmean": ([_vp, _i64, _vp, _int, _i64, _i64, _vp, _sz, _vp], _int),
     "gptq_awq_workspace_size": ([_i64, _i64], _sz),
@@ -283,6 +286,24 @@ def mlp_forward(X, gate, up, bits: int, group: int, Y=None, ws=None, stream=None
                                   bits, group, Y.data_ptr(), Y.stride(0), ws.data_ptr(),
                                   ws.numel() * ws.element_size(), _stream_handle(stream)))
     return Y
+
+
+def dequant_matmul(qweight, scales, zeros, x, bits: int, group: int, d_col: int, y=None,
+                   ws=None, stream=None):
+    """y [n x d_row] float32 = x W^T over the packed layer on the matrix cores, for fp16 x
+    [n x d_col] with 16-byte aligned rows (gptq_dequant_matmul)."""
+    torch = _torch()
+    d_row = qweight.shape[0]
+    n = x.shape[0]
+    assert x.dtype == torch.float16 and x.stride(1) == 1 and x.shape[1] == d_col
+    if y is None:
+        y = torch.empty((n, d_row), dtype=torch.float32, device=x.device)
+    ws = _workspace(lib().gptq_dequant_matmul_workspace_size(d_row, d_col), x.device, ws)
+    _check(lib().gptq_dequant_matmul(qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), d_row,
+                                     d_col, bits, group, x.data_ptr(), n, x.stride(0), y.data_ptr(),
+                                     y.stride(0), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                     _stream_handle(stream)))
+    return y
 
 
 def rmsnorm(x, gamma, eps: float = 1e-6, y=None, stream=None):

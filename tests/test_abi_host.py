@@ -266,3 +266,23 @@ def test_attention_half_validation(lib):
     assert res(ldh=64) == G.EINVAL
     assert res(wsz=ws2 - 1) == G.ENOWS
     assert res(n=0) == G.OK
+
+
+def test_dequant_matmul_validation(lib):
+    f = lib.gptq_dequant_matmul
+    ws = lib.gptq_dequant_matmul_workspace_size(512, 1024)
+    assert ws >= 512 * 1024 * 2                    # the codes as fp16 integers
+    assert lib.gptq_dequant_matmul_workspace_size(512, 1000) == 0
+
+    def call(n=100, d_row=512, d_col=1024, bits=4, group=128, ldx=1024, ldy=512, wsz=ws, x=FAKE):
+        return f(FAKE, FAKE, FAKE, d_row, d_col, bits, group, x, n, ldx, FAKE, ldy, FAKE, wsz, None)
+
+    assert call(bits=6) == G.EINVAL
+    assert call(group=24) == G.EINVAL
+    assert call(d_col=1000, ldx=1000) == G.EINVAL
+    assert call(ldx=1028) == G.EINVAL              # not a multiple of 8
+    assert call(ldy=500) == G.EINVAL
+    assert call(x=ctypes.c_void_p(0x10008)) == G.EINVAL
+    assert call(n=-1) == G.EINVAL
+    assert call(wsz=ws - 1) == G.ENOWS
+    assert call(n=0) == G.OK
