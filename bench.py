@@ -224,7 +224,7 @@ def block_leg(G, torch, Xd, spec, seq_len=2048, d_ff=11008):
     the quantized q/k/v, gate/up_proj on rmsnorm of the residual, down_proj on the MLP product
     of the quantized gate/up), with random fp16 weights ~ N(0, 0.02^2) and norm weights
     exp(0.2 N(0, 1)).  Wall time from events on the launch stream, the time of each kernel
-    family, and the attention kernel against the fp32 vector peak (2 * 128 * l (l + 1) flops
+    family, and the attention kernel against the fp32 MFMA peak (2 * 128 * l (l + 1) flops
     per head and sequence of l tokens: q.k and p.v over the causal pairs) and the forward
     products (fp16 activations times the codes as fp16 integers, 2 n_tok d (4 d + 2 d_ff)
     flops) against the fp16 MFMA peak."""
@@ -272,8 +272,8 @@ def block_leg(G, torch, Xd, spec, seq_len=2048, d_ff=11008):
                       "block": spec.block},
            "ms": ms, "weights": weights, "weights_per_s": weights / (ms / 1e3),
            "families_ms": fams,
-           "attention": {"launches": n_a, "ms": ms_a, "achieved": attn_tf, "peak": 157.3,
-                         "unit": "TFLOP/s", "bound": "alu", "frac": attn_tf / 157.3},
+           "attention": {"launches": n_a, "ms": ms_a, "achieved": attn_tf, "peak": PEAK["mfma_f32"],
+                         "unit": "TFLOP/s", "bound": "mfma", "frac": attn_tf / PEAK["mfma_f32"]},
            "forward_gemm": {"ms": ms_f, "achieved": fwd_tf, "peak": PEAK["mfma_f16"],
                             "unit": "TFLOP/s", "frac": fwd_tf / PEAK["mfma_f16"]},
            "losses": {k: r["loss_" + k] for k in shapes}}

@@ -22,9 +22,6 @@ namespace gptq {
 namespace {
 
 constexpr int HD = ATTN_HEAD_DIM;  // channels per head
-constexpr int AQ = 64;             // queries per workgroup (16 per wave, 4 lanes per query)
-constexpr int AK = 64;             // keys per LDS tile
-constexpr int SLAB = AK * 32;      // floats per 32-channel slab of a tile
 constexpr int64_t TOK_CHUNK = 8192;
 constexpr double ROPE_THETA = 10000.0;
 
@@ -110,142 +107,147 @@ qkv_rope(float* __restrict__ A, int64_t rows, int64_t d, int64_t L,
 }
 
 // ------------------------------------------------------------------ causal attention
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-// sum over the four lanes of a quad (quad_perm [1,0,3,2] then [2,3,0,1])
-__device__ __forceinline__ float quad_sum(float v) {
-  v += dpp<0xB1>(v);
-  return v + dpp<0x4E>(v);
-}
+// One workgroup per (sequence, 128-query tile, head) of a chunk, on the fp32 matrix cores
+// (v_mfma_f32_32x32x2f32: lane l gives A[l%32][l/32] and B[l/32][l%32] and holds
+// C[8(c/4) + 4(l/32) + c%4][l%32] in register c).  Wave w takes the 32 queries
+// w*32 .. w*32 + 31 of the tile; lane l serves query l%32 and keeps its channels
+// 2s + l/32 (s = 0..63) of q in registers.
+//   scores: S^T = K Q^T over 32-key blocks, 64 steps of 2 channels; each lane then holds 16
+//     of its query's 32 scores and the lane l^32 the other 16, so the running maximum and sum
+//     need one swap between the two;
+//   output: O^T += V^T P^T, four 32-channel blocks; step c of a block takes the keys of score
+//     register c (8(c/4) + c%4 and that + 4), so every lane's B operand is its own score
+//     register and nothing moves between lanes.
+// K and V tiles of 64 keys are staged in LDS: K as [key][even channels | odd channels] (a
+// lane's 16-byte read gives four steps), V transposed as [channel][key] (four keys of a
+// block step in one 16-byte read).  Rows are padded by 4 floats.
+constexpr int MQ = 128, MK = 64;
+constexpr int KLD = HD + 4, VLD = MK + 4;
 
-// One workgroup per (sequence, 64-query tile, head) of a chunk.  Lane l of wave w serves
-// query w*16 + l/4 and channels [32 (l%4), 32 (l%4) + 32) of the head: its slice of q, its
-// slice of the output, partial dot products summed over the quad.  Key tiles of 64 keys are
-// staged in LDS as four 32-channel slabs; within a key's 32 floats, slab s is rotated by 8 s
-// floats, so the four addresses a wave reads at once fall in different banks.  The tiles run
-// from the sequence start to the diagonal, with a running maximum and sum (the softmax of the
-// whole row without holding it).
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)
 attn_causal(const float* __restrict__ A, int64_t rows, int64_t d, int64_t L,
             _Float16* __restrict__ O, int64_t ldo) {
-  __shared__ float Ks[4 * SLAB];
-  __shared__ float Vs[4 * SLAB];
+  __shared__ float Ks[MK * KLD];
+  __shared__ float Vt[HD * VLD];
   const int64_t n_heads = d / HD;
   const int64_t n_seq = (rows + L - 1) / L;
-  const int64_t n_qt = ((L < rows ? L : rows) + AQ - 1) / AQ;
+  const int64_t n_qt = ((L < rows ? L : rows) + MQ - 1) / MQ;
   // the longest query tiles (most key tiles) first
   const int64_t b = blockIdx.x;
   const int64_t per_qt = n_heads * n_seq;
   const int64_t qt = n_qt - 1 - b / per_qt;
   const int64_t seq = (b % per_qt) / n_heads;
-  const int64_t h = b % n_heads;
+  const int64_t hd = b % n_heads;
   const int64_t s0 = seq * L;
   const int64_t len = rows - s0 < L ? rows - s0 : L;
-  if (qt * AQ >= len) return;
+  if (qt * MQ >= len) return;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int qi = (tid >> 6) * 16 + (lane >> 2);
-  const int sub = lane & 3;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int j = lane & 31, h = lane >> 5;
   const int64_t ld = 3 * d;
-  const bool valid = qt * AQ + qi < len;
-  const int64_t rq = s0 + qt * AQ + qi;
+  const int64_t q0 = qt * MQ + w * 32;     // the wave's first query
+  const int64_t qj = q0 + j;               // this lane's query
 
-  float q[32];
+  float qreg[64];
   {
-    const float* src = A + (valid ? rq : s0) * ld + h * HD + sub * 32;
+    const float* src = A + (s0 + (qj < len ? qj : len - 1)) * ld + hd * HD + h;
 #pragma unroll
-    for (int c = 0; c < 32; c += 4) {
-      const floatx4 v = *reinterpret_cast<const floatx4*>(src + c);
-      q[c] = v[0]; q[c + 1] = v[1]; q[c + 2] = v[2]; q[c + 3] = v[3];
-    }
+    for (int t = 0; t < 64; ++t) qreg[t] = src[2 * t];
   }
-  float acc[32];
+  floatx16 acc[4];
+  const floatx16 zero16 = {};
 #pragma unroll
-  for (int c = 0; c < 32; ++c) acc[c] = 0.0f;
+  for (int k = 0; k < 4; ++k) acc[k] = zero16;
   float m_run = -INFINITY, l_run = 0.0f;
   const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
 
-  for (int64_t kt = 0; kt <= qt; ++kt) {
+  const int64_t last_q = qt * MQ + MQ - 1 < len - 1 ? qt * MQ + MQ - 1 : len - 1;
+  for (int64_t kt = 0; kt * MK <= last_q; ++kt) {
     __syncthreads();
-    // stage keys [kt*64, kt*64 + 64) of the sequence: 2048 float4 of K and of V
+    // stage keys [kt*64, kt*64 + 64): thread takes key idx % 64 and channels 4 (idx / 64) + 0..3
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int idx = e * 256 + tid;
-      const int j = idx >> 5, c4 = idx & 31;
-      const int slab = c4 >> 3, cc = (c4 & 7) * 4;
-      const int64_t kj = kt * AK + j;
+      const int key = idx & 63, c4 = idx >> 6;
+      const int64_t kj = kt * MK + key;
       floatx4 kv = {0.0f, 0.0f, 0.0f, 0.0f}, vv = {0.0f, 0.0f, 0.0f, 0.0f};
       if (kj < len) {
-        const float* src = A + (s0 + kj) * ld + h * HD + c4 * 4;
+        const float* src = A + (s0 + kj) * ld + hd * HD + c4 * 4;
         kv = *reinterpret_cast<const floatx4*>(src + d);
         vv = *reinterpret_cast<const floatx4*>(src + 2 * d);
       }
-      const int at = slab * SLAB + j * 32 + ((cc + 8 * slab) & 31);
-      *reinterpret_cast<floatx4*>(Ks + at) = kv;
-      *reinterpret_cast<floatx4*>(Vs + at) = vv;
+      float* kr = Ks + key * KLD;
+      kr[2 * c4] = kv[0];
+      kr[2 * c4 + 1] = kv[2];
+      kr[64 + 2 * c4] = kv[1];
+      kr[64 + 2 * c4 + 1] = kv[3];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) Vt[(c4 * 4 + t) * VLD + key] = vv[t];
     }
     __syncthreads();
 
-    // four groups of 16 keys, each folded into the running maximum and sum
-    const float* ks = Ks + sub * SLAB;
-    const float* vs = Vs + sub * SLAB;
-    const int jmax = kt == qt ? qi : AK - 1;  // the last key at or before the query
-#pragma unroll 1
-    for (int j0 = 0; j0 < AK; j0 += 16) {
-      if (j0 > jmax) break;
-      float sc[16];
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const int j = j0 + jj;
-        float part = 0.0f;
+    for (int sub = 0; sub < 2; ++sub) {
+      const int64_t kb = kt * MK + sub * 32;
+      if (kb > q0 + 31) continue;             // every key after every query of the wave
+      floatx16 S = zero16;
+      const float* kp = Ks + (sub * 32 + j) * KLD + h * 64;
 #pragma unroll
-        for (int c = 0; c < 32; c += 4) {
-          const floatx4 k4 = *reinterpret_cast<const floatx4*>(ks + j * 32 + ((c + 8 * sub) & 31));
-          part += q[c] * k4[0] + q[c + 1] * k4[1] + q[c + 2] * k4[2] + q[c + 3] * k4[3];
-        }
-        sc[jj] = j <= jmax ? quad_sum(part) * scale : -INFINITY;
+      for (int s4 = 0; s4 < 16; ++s4) {
+        const floatx4 k4 = *reinterpret_cast<const floatx4*>(kp + 4 * s4);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          S = __builtin_amdgcn_mfma_f32_32x32x2f32(k4[t], qreg[4 * s4 + t], S, 0, 0, 0);
       }
-      float mx = m_run;
+      float mx = -INFINITY;
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, sc[jj]);
-      const float corr = expf(m_run - mx);
-      float psum = 0.0f;
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        sc[jj] = expf(sc[jj] - mx);
-        psum += sc[jj];
+      for (int c = 0; c < 16; ++c) {
+        const int64_t key = kb + 8 * (c >> 2) + 4 * h + (c & 3);
+        S[c] = key <= qj ? S[c] * scale : -INFINITY;
+        mx = fmaxf(mx, S[c]);
       }
-      l_run = l_run * corr + psum;
-      m_run = mx;
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      float ps = 0.0f;
 #pragma unroll
-      for (int c = 0; c < 32; ++c) acc[c] *= corr;
+      for (int c = 0; c < 16; ++c) {
+        S[c] = expf(S[c] - m_new);
+        ps += S[c];
+      }
+      ps += __shfl_xor(ps, 32);
+      const float corr = expf(m_run - m_new);
+      l_run = l_run * corr + ps;
+      m_run = m_new;
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const int j = j0 + jj;
+      for (int k = 0; k < 4; ++k)
 #pragma unroll
-        for (int c = 0; c < 32; c += 4) {
-          const floatx4 v4 = *reinterpret_cast<const floatx4*>(vs + j * 32 + ((c + 8 * sub) & 31));
-          acc[c] += sc[jj] * v4[0];
-          acc[c + 1] += sc[jj] * v4[1];
-          acc[c + 2] += sc[jj] * v4[2];
-          acc[c + 3] += sc[jj] * v4[3];
+        for (int c = 0; c < 16; ++c) acc[k][c] *= corr;
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const float* vp = Vt + (blk * 32 + j) * VLD + sub * 32 + 4 * h;
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) {
+          const floatx4 v4 = *reinterpret_cast<const floatx4*>(vp + 8 * m4);
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            acc[blk] = __builtin_amdgcn_mfma_f32_32x32x2f32(v4[t], S[4 * m4 + t], acc[blk], 0, 0, 0);
         }
       }
     }
   }
-  if (!valid) return;
-  _Float16* dst = O + rq * ldo + h * HD + sub * 32;
+  if (qj >= len) return;
   const float inv = 1.0f / l_run;
+  _Float16* dst = O + (s0 + qj) * ldo + hd * HD;
 #pragma unroll
-  for (int c = 0; c < 32; c += 8) {
-    half8 o;
+  for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) o[k] = (_Float16)(acc[c + k] * inv);
-    *reinterpret_cast<half8*>(dst + c) = o;
-  }
+    for (int m4 = 0; m4 < 4; ++m4) {
+      typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+      half4 o;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) o[t] = (_Float16)(acc[blk][4 * m4 + t] * inv);
+      *reinterpret_cast<half4*>(dst + blk * 32 + 8 * m4 + 4 * h) = o;
+    }
 }
 
 // ------------------------------------------------------------------ residual
@@ -313,7 +315,7 @@ hipError_t attn_launch(const _Float16* X, int64_t n_tok, int64_t d, int64_t ldx,
       hipLaunchKernelGGL(qkv_rope, dim3(grid_of(rows * d / 2)), dim3(256), 0, s, A, rows, d, L, tab);
     }
     const int64_t n_seq = ceil_div(rows, L);
-    const int64_t n_qt = ceil_div(L < rows ? L : rows, AQ);
+    const int64_t n_qt = ceil_div(L < rows ? L : rows, MQ);
     {
       ProfScope ps_("attention", s);
       hipLaunchKernelGGL(attn_causal, dim3((unsigned)(n_qt * n_seq * (d / HD))), dim3(256), 0, s, A,
