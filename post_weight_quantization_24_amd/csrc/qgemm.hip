@@ -160,6 +160,162 @@ qgemm_k(const _Float16* __restrict__ A, int64_t lda, int64_t M, const _Float16* 
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// The same product through a ring of three K stages filled by direct-to-LDS copies, for
+// groups that are whole stages (g % 64 == 0, K % 64 == 0): every production layer.
+// Eight waves in a 2 x 4 grid own 64 x 64 outputs each of a 128 x 256 tile.  A stage holds
+// 128 rows of A and 256 rows of B, 64 halfs (128 bytes) per row, 48 KB; the copies of stage
+// s + 2 are issued while stage s is multiplied, so loads run two stages ahead without
+// staging registers.  In a row the 16-byte slots are XOR-swizzled by (row / 2) % 8, so the
+// 16 rows that a fragment read serves at once fall in distinct banks.  Rows past M or N
+// read as zero (the buffer ends there).
+
+constexpr int DM = 128, DN = 256, DK = 64, DNST = 3;
+constexpr int DROW = DK * 2;                              // bytes per row and stage
+constexpr int DA_BYTES = DM * DROW, DB_BYTES = DN * DROW;
+constexpr int DSTAGE = DA_BYTES + DB_BYTES;               // 48 KB
+constexpr int DWAVES = 8;
+constexpr int DCPW = (DM + DN) * DROW / 1024 / DWAVES;    // 1 KB copies per wave and stage: 6
+
+typedef uint32_t rsrc_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int dswz(int row, int slot) { return slot ^ ((row >> 1) & 7); }
+
+// One wave-wide 1 KB copy global -> LDS: lane l's 16 bytes at buffer offset voff land at
+// lds_base + 16 l.  No register output; the explicit vmcnt waits order the copies.
+__device__ __forceinline__ void dcopy(rsrc_t rsrc, uint32_t lds_base, int voff) {
+  __asm__ volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                   :
+                   : "v"(voff), "s"(rsrc), "s"(lds_base)
+                   : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void dwait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// barrier without __syncthreads' fence (which would drain the copies meant to stay in flight)
+__device__ __forceinline__ void dbarrier() {
+  __builtin_amdgcn_s_waitcnt((15 & 15) | (3 << 14) | (7 << 4) | (0 << 8));
+  __builtin_amdgcn_s_barrier();
+}
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t nbytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane((uint32_t)nbytes);
+  const rsrc_t r = {lo, hi & 0xffffu, n, 0x00020000u};
+  return r;
+}
+
+__global__ void __launch_bounds__(64 * DWAVES, 1)
+qgemm_dma(const _Float16* __restrict__ A, int64_t lda, int64_t M, const _Float16* __restrict__ B,
+          int64_t N, int64_t K, const float* __restrict__ S, int64_t n_groups, int spg,
+          float* __restrict__ C, int64_t ldc) {
+  __shared__ __attribute__((aligned(16))) char lds[DNST * DSTAGE];
+  const int64_t tiles_m = (M + DM - 1) / DM;
+  const int64_t tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+  const int64_t m0 = tm * DM, n0 = tn * DN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int li = lane & 31, lh = lane >> 5;
+  const int64_t rows_a = M - m0 < DM ? M - m0 : DM;
+  const int64_t rows_b = N - n0 < DN ? N - n0 : DN;
+  const rsrc_t ra = make_rsrc(A + m0 * lda, rows_a * lda * 2);
+  const rsrc_t rb = make_rsrc(B + n0 * K, rows_b * K * 2);
+  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)lds);
+
+  // copy c (0 .. DCPW - 1) of this wave for stage st: copy q = wave * DCPW + c covers rows
+  // 8 q' .. 8 q' + 7 of A (q < 16, q' = q) or of B (q' = q - 16)
+  auto issue = [&](int64_t st) {
+    const uint32_t sbase = lds0 + (uint32_t)((st % DNST) * DSTAGE);
+#pragma unroll
+    for (int c = 0; c < DCPW; ++c) {
+      const int q = wave * DCPW + c;
+      const bool isa = q < DM / 8;
+      const int qq = isa ? q : q - DM / 8;
+      const int row = 8 * qq + (lane >> 3);
+      const int lslot = dswz(row, lane & 7);
+      const int64_t ld = isa ? lda : K;
+      const int voff = (int)((row * ld + st * DK + 8 * lslot) * 2);
+      dcopy(isa ? ra : rb, sbase + (isa ? 0u : (uint32_t)DA_BYTES) + (uint32_t)qq * 1024u, voff);
+    }
+  };
+
+  floatx16 acc[2][2], part[2][2];
+  const floatx16 zero16 = {};
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = part[a][b] = zero16;
+  const int64_t col0 = n0 + wn * 64 + li, col1 = col0 + 32;
+  const float* s0 = S + (col0 < N ? col0 : N - 1) * n_groups;
+  const float* s1 = S + (col1 < N ? col1 : N - 1) * n_groups;
+  float sc0 = s0[0], sc1 = s1[0];
+  int64_t grp = 0;
+
+  const int64_t nst = K / DK;
+  issue(0);
+  if (nst > 1) issue(1);
+  for (int64_t st = 0; st < nst; ++st) {
+    if (st + 1 < nst) dwait_vmcnt<DCPW>();
+    else dwait_vmcnt<0>();
+    dbarrier();
+    if (st + 2 < nst) issue(st + 2);
+    const char* sb = lds + (st % DNST) * DSTAGE;
+    const bool fresh = st % spg == 0;
+#pragma unroll
+    for (int kk = 0; kk < DK / 16; ++kk) {
+      const int lslot = 2 * kk + lh;
+      half8 af[2], bf[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const int row = wm * 64 + a * 32 + li;
+        af[a] = *reinterpret_cast<const half8*>(sb + row * DROW + 16 * dswz(row, lslot));
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int row = wn * 64 + b * 32 + li;
+        bf[b] = *reinterpret_cast<const half8*>(sb + DA_BYTES + row * DROW + 16 * dswz(row, lslot));
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          part[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              af[a], bf[b], fresh && kk == 0 ? zero16 : part[a][b], 0, 0, 0);
+    }
+    if ((st + 1) % spg == 0) {            // the group ends with this stage
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          acc[a][0][c] += sc0 * part[a][0][c];
+          acc[a][1][c] += sc1 * part[a][1][c];
+        }
+      ++grp;
+      if (grp < n_groups) {
+        sc0 = s0[grp];
+        sc1 = s1[grp];
+      }
+    }
+  }
+
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t col = n0 + wn * 64 + b * 32 + li;
+      if (col >= N) continue;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const int64_t row = m0 + wm * 64 + a * 32 + 8 * (c >> 2) + 4 * lh + (c & 3);
+        if (row < M) C[row * ldc + col] = acc[a][b][c];
+      }
+    }
+}
+
 }  // namespace
 
 void expand_codes_f16(const uint32_t* q, const uint8_t* z, int64_t N, int64_t K, int bits,
@@ -174,6 +330,13 @@ hipError_t qgemm_f16(const _Float16* A, int64_t lda, int64_t M, const _Float16* 
                      const char* prof_name) {
   if (M <= 0 || N <= 0) return hipSuccess;
   ProfScope ps(prof_name, s);
+  if (g % DK == 0 && K % DK == 0 && (int64_t)DM * lda * 2 < ((int64_t)1 << 31) &&
+      (int64_t)DN * K * 2 < ((int64_t)1 << 31)) {
+    const int64_t tiles = ceil_div(M, DM) * ceil_div(N, DN);
+    hipLaunchKernelGGL(qgemm_dma, dim3((unsigned)tiles), dim3(64 * DWAVES), 0, s, A, lda, M, B, N, K,
+                       S, K / g, (int)(g / DK), C, ldc);
+    return hipGetLastError();
+  }
   const int64_t tiles = ceil_div(M, QM) * ceil_div(N, QN);
   hipLaunchKernelGGL(qgemm_k, dim3((unsigned)tiles), dim3(256), 0, s, A, lda, M, B, N, K, S, K / g,
                      (int)(g / 16), C, ldc);
