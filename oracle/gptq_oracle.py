@@ -72,6 +72,16 @@ INT2), the hand-solved 1x2 layer, and sum_t ||W x_t - y_t||^2 = 1/2 sum_r D_r H 
 obq_greedy_quantize (tests/test_oracle_obq.py): a brute-force greedy by least squares on
 the token matrix (order, codes and W^), the literal OBS step in the greedy's own order,
 and H proportional to I giving round-to-nearest.
+act_absmean, awq_alphas, awq_scales, awq_search (tests/test_oracle_awq.py): a per-token loop
+for s_X, the grid's end points, alpha = 0 or flat s_X giving round-to-nearest bit for bit,
+every grid loss equal to the output error summed over tokens, the salient-channel effect.
+silu, mlp_forward, mlp_block (tests/test_oracle_mlp.py): silu's closed forms, the product
+against scalar loops over the code integers, the chain's wiring and its direct-sum losses.
+rmsnorm, rope, causal_attention, attn_forward, residual_linear, decoder_block
+(tests/test_oracle_block.py): a constant token in closed form and scale invariance, rope on
+a unit vector and against its complex form, attention in closed form on head_dim 2, zero
+queries giving the running mean, causality, independent sequences, packed identity and
+zero weights, the chain's wiring.
 No function here is "parity unpinned".
 """
 
