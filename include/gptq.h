@@ -140,7 +140,10 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t d_row, int64_t d_col
  * Dequantizes W^ = s * (code - z) and measures the layer objective of page "量化", GPTQ,
  * ||W X - W^ X||_F^2 = 1/2 * sum_r (W - W^)_r H (W - W^)_r^T with the undamped H.
  *   qweight/scales/zeros  as written by gptq_quantize_layer for the same spec and shape.
- *   W        the original weights; H the undamped d_col x d_col Hessian.
+ *   W        the original weights; H the undamped d_col x d_col Hessian (symmetric, as
+ *            gptq_hessian_accumulate writes it: only its upper triangle is read; the loss
+ *            is formed from the half product T = D U, U that triangle, as
+ *            sum_c T D - 1/2 sum_c D^2 H_cc per row, in double).
  *   loss     device pointer to 1 double (the objective above).
  *   row_loss NULL or device pointer to d_row doubles (each row's share).
  *   W_hat    NULL or device d_row x d_col float32 receiving the dequantized weights.

@@ -49,19 +49,6 @@ grid_check(const float* __restrict__ scales, const uint8_t* __restrict__ zeros, 
 
 __global__ void zero_i64(unsigned long long* p) { *p = 0ull; }
 
-// One wave per row: 1/2 * sum_c T[r][c] * D[r][c] in double.
-__global__ void __launch_bounds__(256)
-row_loss_k(const float* __restrict__ T, const float* __restrict__ D, int64_t d_row, int64_t d_col,
-           double* __restrict__ rows) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= d_row) return;
-  double acc = 0.0;
-  for (int64_t c = lane; c < d_col; c += 64) acc += (double)T[r * d_col + c] * (double)D[r * d_col + c];
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (lane == 0) rows[r] = 0.5 * acc;
-}
-
 // One wave per row, for T = D U with U the upper triangle of H (diagonal included):
 // 1/2 D_r H D_r^T = sum_c T[r][c] D[r][c] - 1/2 sum_c D[r][c]^2 H[c][c], in double.
 __global__ void __launch_bounds__(256)
@@ -126,7 +113,7 @@ hipError_t check_launch(const uint32_t* qweight, const float* scales, const uint
                      dim3(256), 0, s, scales, zeros, ng, bits, og);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return loss_of_diff(D, H, d_row, d_col, loss, row_loss, T, rows, s, "check_gemm");
+  return loss_of_diff_upper(D, H, d_row, d_col, loss, row_loss, T, rows, s, "check_gemm");
 }
 
 hipError_t loss_of_diff_upper(const float* D, const float* H, int64_t d_row, int64_t d_col,
@@ -142,16 +129,5 @@ hipError_t loss_of_diff_upper(const float* D, const float* H, int64_t d_row, int
   return hipGetLastError();
 }
 
-hipError_t loss_of_diff(const float* D, const float* H, int64_t d_row, int64_t d_col, double* loss,
-                        double* row_loss, float* T, double* rows, hipStream_t s,
-                        const char* prof_name) {
-  GemmArgs ga{d_row, d_col, d_col, D, d_col, 0, 0, H, d_col, 0, 0, T, d_col, 0, 1.0f, 0.0f};
-  hipError_t e = gemm_f32(ga, s, prof_name);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(row_loss_k, dim3((unsigned)ceil_div(d_row, 4)), dim3(256), 0, s, T, D, d_row,
-                     d_col, rows);
-  hipLaunchKernelGGL(sum_rows, dim3(1), dim3(256), 0, s, rows, d_row, loss, row_loss);
-  return hipGetLastError();
-}
 
 }  // namespace gptq

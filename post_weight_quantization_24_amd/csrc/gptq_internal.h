@@ -78,11 +78,6 @@ hipError_t check_launch(const uint32_t* qweight, const float* scales, const uint
                         int bits, int group, double* loss, double* row_loss, float* W_hat,
                         int64_t* off_grid, void* ws, hipStream_t stream);
 
-// loss = 1/2 sum_r D_r H D_r^T (and its rows) for D [d_row x d_col]; T [d_row x d_col] and
-// rows [d_row] are scratch.  Sums in double, in a fixed order.
-hipError_t loss_of_diff(const float* D, const float* H, int64_t d_row, int64_t d_col, double* loss,
-                        double* row_loss, float* T, double* rows, hipStream_t s,
-                        const char* prof_name);
 // The same loss for a symmetric H from half the product: T = D U with U the upper triangle
 // of H (diagonal included), then sum_c T D - 1/2 sum_c D^2 H_cc per row.
 hipError_t loss_of_diff_upper(const float* D, const float* H, int64_t d_row, int64_t d_col,
