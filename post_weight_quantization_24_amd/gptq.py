@@ -310,6 +310,7 @@ def rmsnorm(x, gamma, eps: float = 1e-6, y=None, stream=None):
     """y [n_tok x d] fp16 = x / sqrt(mean(x^2) + eps) * gamma per token (gptq_rmsnorm)."""
     torch = _torch()
     n_tok, d = x.shape
+    assert x.dtype == torch.float16 and gamma.dtype == torch.float16, "rmsnorm takes fp16"
     assert x.stride(1) == 1 and gamma.is_contiguous() and gamma.numel() == d
     if y is None:
         y = torch.empty((n_tok, d), dtype=torch.float16, device=x.device)
@@ -324,6 +325,7 @@ def attention_forward(X, q, k, v, bits: int, group: int, seq_len: int, O=None, w
     tokens, on q, k, v = X W^T from the packed q/k/v layers (gptq_attention_forward)."""
     torch = _torch()
     n_tok, d = X.shape
+    assert X.dtype == torch.float16, "attention_forward takes fp16 X"
     assert X.stride(1) == 1 and all(p[0].shape[0] == d for p in (q, k, v))
     if O is None:
         O = torch.empty((n_tok, d), dtype=torch.float16, device=X.device)
@@ -341,6 +343,7 @@ def residual_linear(X, R, layer, bits: int, group: int, out=None, ws=None, strea
     torch = _torch()
     n_tok, d_in = X.shape
     d_out = layer[0].shape[0]
+    assert X.dtype == torch.float16 and R.dtype == torch.float16, "residual_linear takes fp16"
     assert X.stride(1) == 1 and R.stride(1) == 1 and R.shape == (n_tok, d_out)
     if out is None:
         out = torch.empty((n_tok, d_out), dtype=torch.float16, device=X.device)
