@@ -45,6 +45,47 @@ expand_codes(const uint32_t* __restrict__ qweight, const uint8_t* __restrict__ z
   }
 }
 
+// The same for 2-, 4- and 8-bit codes, one 32-bit word per thread: its 32 / BITS codes are
+// consecutive columns of one group (g is a multiple of 16), so one zero point serves them,
+// and they are written as one or two 16-byte (or one 8-byte) stores.
+template <int BITS>
+__global__ void __launch_bounds__(256)
+expand_words(const uint32_t* __restrict__ qweight, const uint8_t* __restrict__ zeros, int64_t N,
+             int64_t K, int64_t g, _Float16* __restrict__ B) {
+  constexpr int PER = 32 / BITS;
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
+  const int64_t wpr = K / PER;
+  const int64_t n = N * wpr;
+  const int64_t n_groups = K / g;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / wpr, c0 = (i - r * wpr) * PER;
+    const uint32_t wv = qweight[i];
+    const float z = (float)zeros[r * n_groups + c0 / g];
+    _Float16 o[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) o[k] = (_Float16)((float)((wv >> (BITS * k)) & MASK) - z);
+    _Float16* dst = B + r * K + c0;
+    if constexpr (PER == 16) {
+      half8 a, b;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) { a[k] = o[k]; b[k] = o[8 + k]; }
+      reinterpret_cast<half8*>(dst)[0] = a;
+      reinterpret_cast<half8*>(dst)[1] = b;
+    } else if constexpr (PER == 8) {
+      half8 a;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) a[k] = o[k];
+      *reinterpret_cast<half8*>(dst) = a;
+    } else {
+      typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+      half4 a;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) a[k] = o[k];
+      *reinterpret_cast<half4*>(dst) = a;
+    }
+  }
+}
+
 __global__ void __launch_bounds__(256, 2)
 qgemm_k(const _Float16* __restrict__ A, int64_t lda, int64_t M, const _Float16* __restrict__ B,
         int64_t N, int64_t K, const float* __restrict__ S, int64_t n_groups, int gsteps,
@@ -320,6 +361,15 @@ qgemm_dma(const _Float16* __restrict__ A, int64_t lda, int64_t M, const _Float16
 
 void expand_codes_f16(const uint32_t* q, const uint8_t* z, int64_t N, int64_t K, int bits,
                       int64_t g, _Float16* B, hipStream_t s) {
+  if (bits != 3) {
+    const int64_t words = N * K * bits / 32;
+    const int64_t wb = ceil_div(words, 256);
+    const dim3 grid((unsigned)(wb < 16384 ? wb : 16384));
+    if (bits == 4) hipLaunchKernelGGL(expand_words<4>, grid, dim3(256), 0, s, q, z, N, K, g, B);
+    else if (bits == 2) hipLaunchKernelGGL(expand_words<2>, grid, dim3(256), 0, s, q, z, N, K, g, B);
+    else hipLaunchKernelGGL(expand_words<8>, grid, dim3(256), 0, s, q, z, N, K, g, B);
+    return;
+  }
   const int64_t blocks = ceil_div(N * K, 256);
   hipLaunchKernelGGL(expand_codes, dim3((unsigned)(blocks < 16384 ? blocks : 16384)), dim3(256), 0,
                      s, q, z, N, K, bits, g, B);
