@@ -317,8 +317,9 @@ int gptq_residual_linear(const void* X, int64_t n_tok, int64_t d_in, int64_t ldx
  * Optional per-kernel timing with HIP events recorded on the caller's stream around
  * every launch of the named kernel family ("hessian_mfma", "hessian_reduce", "prep_leaf",
  * "prep_gemm", "quant_block", "lazy_gemm", "dequant_matvec", "absmean", "awq_scale_rtn",
- * "awq_gemm", "mlp_gemm", "mlp_elementwise", ...).  Enabling costs two event records per
- * timed launch; gptq_profile_only(name) restricts timing to one family (NULL: all).
+ * "awq_gemm", "mlp_gemm", "mlp_elementwise", "block_gemm", "block_elementwise", "attention",
+ * "dequant_expand", "dequant_matmul", "check", "check_gemm", ...).  Enabling costs two event
+ * records per timed launch; gptq_profile_only(name) restricts timing to one family (NULL: all).
  * gptq_profile_read returns the number of timed launches and their summed duration in
  * milliseconds (waits for the recorded events).  For measurement, not for production. */
 int gptq_profile_enable(int on);
