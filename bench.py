@@ -318,9 +318,8 @@ def cpu_baseline(W, X_sample, n_tok_full, spec, rows):
 def main():
     a = parse()
     if a.gpus != 1:
-        print("bench.py: this build runs on one GPU; --gpus %d is not supported (the layer "
-              "shards by output rows and by token ranges, see the design notes)" % a.gpus,
-              file=sys.stderr)
+        print("bench.py: measures one GPU; --gpus %d is not supported (across GPUs the layer "
+              "would shard by output rows and by token ranges)" % a.gpus, file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
