@@ -152,20 +152,21 @@ def _mlp_tol(X, gate, up, bits, group, d):
     return _step(y) + 1.1 * np.abs(b) * ea + (np.abs(a) + 1.0) * eb + 4e-6 * np.abs(y)
 
 
-def test_decoder_block_chain():
+@pytest.mark.parametrize("n,L,bits,group,sym,B", [(2048, 512, 4, 128, False, 128),
+                                                  (2300, 512, 3, 64, True, 64)])
+def test_decoder_block_chain(n, L, bits, group, sym, B):
     """Stage by stage: every calibration input the GPU forms is checked against the oracle's
     forward pass of the GPU's own previous input and quantized layers (within the bounds
     above), and every sub-layer's codes against the oracle's column solve on the GPU's own
     input (the parity bar of the column solve).  End to end, each layer loss is compared
     with the oracle's whole chain run on its own."""
     torch = _torch()
-    say("decoder block chain")
-    n, d, d_ff, L = 2048, 256, 512, 512
-    bits, group, sym, B, damp = 4, 128, False, 128, 0.01
+    say("decoder block chain", n, L, bits, group, sym, B)
+    d, d_ff, damp = 256, 512, 0.01
     shapes = {"q_proj": (d, d), "k_proj": (d, d), "v_proj": (d, d), "o_proj": (d, d),
               "gate_proj": (d_ff, d), "up_proj": (d_ff, d), "down_proj": (d, d_ff)}
-    W = {k: synth.gen_weight(1000, k, r, c, 0.05, "f16") for k, (r, c) in shapes.items()}
-    x = synth.gen_acts(1000, "x", n, d, "f16")
+    W = {k: synth.gen_weight(1000 + bits, k, r, c, 0.05, "f16") for k, (r, c) in shapes.items()}
+    x = synth.gen_acts(1000 + bits, "x", n, d, "f16")
     g1, g2 = synth.gen_norm_weight(1000, "g1", d), synth.gen_norm_weight(1000, "g2", d)
     spec = G.Spec.make(bits, group, sym, B, damp)
     r = BLK.quantize_decoder_block({k: to_dev(w) for k, w in W.items()}, to_dev(x), to_dev(g1),
