@@ -69,3 +69,37 @@ def test_dequant_matmul_matches_matvec():
     err = (a - b).abs().cpu().numpy()
     say("max difference / bound %.3g" % float((err / tol).max()))
     assert np.all(err <= tol)
+
+
+@pytest.mark.slow
+def test_dequant_matmul_70b_shape_sampled():
+    """The bench's batched case (gate_proj 28672 x 8192 INT4 g128 at 2048 rows, the launch
+    configuration bench.py times) on sampled outputs, each computed by the oracle from its
+    row of codes and its activation row."""
+    torch = _torch()
+    say("dequant_matmul 70B shape, sampled")
+    d_row, d_col, bits, group, n = 28672, 8192, 4, 128, 2048
+    rng = np.random.default_rng(1040)
+    # uniformly random words are uniformly random 4-bit codes (as the bench draws them)
+    words = rng.integers(0, 1 << 32, (d_row, d_col * bits // 32), dtype=np.uint64).astype(np.uint32)
+    scales = rng.uniform(0.002, 0.02, (d_row, d_col // group)).astype(np.float32)
+    zeros = rng.integers(0, 1 << bits, (d_row, d_col // group)).astype(np.uint8)
+    x = acts(rng, n, d_col)
+    dev = "cuda:0"
+    y = G.dequant_matmul(torch.from_numpy(words.view(np.int32)).to(dev),
+                         torch.from_numpy(scales).to(dev), torch.from_numpy(zeros).to(dev),
+                         torch.from_numpy(x).to(dev), bits, group, d_col)
+    torch.cuda.synchronize()
+    rows = rng.integers(0, d_row, 64)
+    toks = rng.integers(0, n, 64)
+    got = y[torch.from_numpy(toks).to(dev), torch.from_numpy(rows).to(dev)].cpu().numpy()
+    worst = 0.0
+    for t, r, v in zip(toks, rows, got):
+        ref = O.dequant_matvec(words[r:r + 1], scales[r:r + 1], zeros[r:r + 1], bits, group, d_col,
+                               x[t:t + 1])[0, 0]
+        wh = O.dequantize(O.unpack_codes(words[r:r + 1], bits, d_col), scales[r:r + 1],
+                          zeros[r:r + 1], group)[0]
+        tol = 2.0 ** -24 * (group + d_col / group + 4) * float(np.abs(x[t].astype(np.float64)) @ np.abs(wh))
+        worst = max(worst, abs(float(v) - ref) / tol)
+        assert abs(float(v) - ref) <= tol, (t, r)
+    say("max err / tol over 64 samples %.3g" % worst)
