@@ -7,7 +7,9 @@ If libgptq.so is missing the first call raises: there is no other implementation
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
 import os
 import re
 from typing import Optional
@@ -58,6 +60,7 @@ _SIGS = {
                              _vp, _sz, _vp], _int),
     "gptq_act_absmean_workspace_size": ([_i64, _i64], _sz),
     "gptq_act_absmean": ([_vp, _i64, _vp, _int, _i64, _i64, _vp, _sz, _vp], _int),
+    "gptq_act_absmean_noalloc": ([_vp, _i64, _vp, _int, _i64, _i64, _vp], _int),
     "gptq_awq_workspace_size": ([_i64, _i64], _sz),
     "gptq_awq_search": ([_vp, _int, _i64, _i64, _vp, _vp, _i64, ctypes.POINTER(Spec), _int, _vp,
                          _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
@@ -128,6 +131,44 @@ def _stream_handle(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+@contextlib.contextmanager
+def _on_stream(stream, *tensors):
+    """Runs one call on `stream` (None: torch's current stream, nothing to do).
+
+    For another stream: that stream first waits for the work already queued on the current
+    stream (which produced the inputs or zero-filled the accumulators); every tensor the call
+    touches is marked as used on it (record_stream), so the caching allocator does not hand
+    its memory out again before the call's kernels have finished; and the call's own outputs
+    and workspaces are allocated under it, so they belong to that stream."""
+    torch = _torch()
+    if stream is None:
+        yield
+        return
+    cur = torch.cuda.current_stream()
+    if stream != cur:
+        stream.wait_stream(cur)
+        for t in tensors:
+            if t is not None and t.is_cuda:
+                t.record_stream(stream)
+    with torch.cuda.stream(stream):
+        yield
+
+
+def _streamed(fn):
+    """Wraps a binding call taking `stream=` in _on_stream with every tensor argument (also
+    those inside tuples, such as a packed layer)."""
+    @functools.wraps(fn)
+    def call(*args, stream=None, **kw):
+        tensors = []
+        for a in list(args) + list(kw.values()):
+            for t in (a if isinstance(a, (tuple, list)) else (a,)):
+                if hasattr(t, "record_stream"):
+                    tensors.append(t)
+        with _on_stream(stream, *tensors):
+            return fn(*args, stream=stream, **kw)
+    return call
+
+
 def _dtype_code(t) -> int:
     torch = _torch()
     if t.dtype == torch.float16:
@@ -144,6 +185,7 @@ def _workspace(nbytes: int, device, ws=None):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
+@_streamed
 def hessian_accumulate(H, X, ws=None, stream=None):
     """H += 2 X^T X for X [n_tok, d] (rows may be strided); H [d, d] float32."""
     d = H.shape[0]
@@ -159,6 +201,7 @@ def hessian_accumulate(H, X, ws=None, stream=None):
     return H
 
 
+@_streamed
 def prepare_hinv(H, G=None, damp_frac=0.01, ws=None, check=True, stream=None):
     """G = Cholesky((H + lambda I)^-1)^T.  check=True waits and raises on a bad pivot."""
     torch = _torch()
@@ -174,6 +217,7 @@ def prepare_hinv(H, G=None, damp_frac=0.01, ws=None, check=True, stream=None):
     return G
 
 
+@_streamed
 def quantize_layer(W, G, spec: Spec, qweight=None, scales=None, zeros=None, err_sq=True,
                    ws=None, stream=None):
     """Returns (qweight int32 view of the uint32 words, scales, zeros uint8, err_sq_rows)."""
@@ -200,6 +244,7 @@ def quantize_layer(W, G, spec: Spec, qweight=None, scales=None, zeros=None, err_
     return qweight, scales, zeros, esq
 
 
+@_streamed
 def dequant_check(qweight, scales, zeros, W, H, spec: Spec, want_w_hat=False, ws=None, stream=None):
     """Returns (loss float64[1], row_loss float64[d_row], W_hat or None, off_grid int64[1])."""
     torch = _torch()
@@ -219,6 +264,7 @@ def dequant_check(qweight, scales, zeros, W, H, spec: Spec, want_w_hat=False, ws
     return loss, row_loss, w_hat, off
 
 
+@_streamed
 def dequant_matvec(qweight, scales, zeros, x, bits: int, group: int, d_col: int, y=None,
                    stream=None):
     """y [n x d_row] fp32 = x [n x d_col] fp16 times the dequantized packed weights, transposed
@@ -235,6 +281,7 @@ def dequant_matvec(qweight, scales, zeros, x, bits: int, group: int, d_col: int,
     return y
 
 
+@_streamed
 def act_absmean(sx_sum, X, ws=None, stream=None):
     """sx_sum [d] float64 += sum over the rows of X [n_tok, d] of |x| (gptq_act_absmean)."""
     d = sx_sum.shape[0]
@@ -247,6 +294,18 @@ def act_absmean(sx_sum, X, ws=None, stream=None):
     return sx_sum
 
 
+@_streamed
+def act_absmean_noalloc(sx_sum, X, stream=None):
+    """sx_sum [d] float64 += sum over the rows of X of |x|, with the library's own scratch
+    (gptq_act_absmean_noalloc: no workspace, nothing allocated)."""
+    d = sx_sum.shape[0]
+    assert X.dim() == 2 and X.shape[1] == d and X.stride(1) == 1 and sx_sum.is_contiguous()
+    _check(lib().gptq_act_absmean_noalloc(sx_sum.data_ptr(), d, X.data_ptr(), _dtype_code(X),
+                                          X.shape[0], X.stride(0), _stream_handle(stream)))
+    return sx_sum
+
+
+@_streamed
 def awq_search(W, H, sx_sum, n_tok: int, spec: Spec, n_grid: int = 20, ws=None, stream=None):
     """Returns (qweight, scales, zeros, s [d_col] float32, losses [n_grid] float64,
     best int32[1]) of gptq_awq_search."""
@@ -270,6 +329,7 @@ def awq_search(W, H, sx_sum, n_tok: int, spec: Spec, n_grid: int = 20, ws=None, 
     return qweight, scales, zeros, s, losses, best
 
 
+@_streamed
 def mlp_forward(X, gate, up, bits: int, group: int, Y=None, ws=None, stream=None):
     """Y [n_tok x d_ff] fp16 = silu(X G^T) * (X U^T) from packed gate and up layers, each
     (qweight, scales, zeros) as quantize_layer returns them (gptq_mlp_forward)."""
@@ -288,6 +348,7 @@ def mlp_forward(X, gate, up, bits: int, group: int, Y=None, ws=None, stream=None
     return Y
 
 
+@_streamed
 def dequant_matmul(qweight, scales, zeros, x, bits: int, group: int, d_col: int, y=None,
                    ws=None, stream=None):
     """y [n x d_row] float32 = x W^T over the packed layer on the matrix cores, for fp16 x
@@ -306,6 +367,7 @@ def dequant_matmul(qweight, scales, zeros, x, bits: int, group: int, d_col: int,
     return y
 
 
+@_streamed
 def rmsnorm(x, gamma, eps: float = 1e-6, y=None, stream=None):
     """y [n_tok x d] fp16 = x / sqrt(mean(x^2) + eps) * gamma per token (gptq_rmsnorm)."""
     torch = _torch()
@@ -319,6 +381,7 @@ def rmsnorm(x, gamma, eps: float = 1e-6, y=None, stream=None):
     return y
 
 
+@_streamed
 def attention_forward(X, q, k, v, bits: int, group: int, seq_len: int, O=None, ws=None,
                       stream=None):
     """O [n_tok x d] fp16: causal attention with rotary embedding over sequences of seq_len
@@ -338,6 +401,7 @@ def attention_forward(X, q, k, v, bits: int, group: int, seq_len: int, O=None, w
     return O
 
 
+@_streamed
 def residual_linear(X, R, layer, bits: int, group: int, out=None, ws=None, stream=None):
     """out [n_tok x d_out] fp16 = R + X W^T for one packed layer (gptq_residual_linear)."""
     torch = _torch()

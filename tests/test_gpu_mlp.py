@@ -105,3 +105,28 @@ def test_mlp_block_chain():
     say("down", st)
     for k in ("loss_gate", "loss_up", "loss_down"):
         assert abs(r[k] - o[k]) <= 5e-3 * o[k], (k, r[k], o[k])
+
+
+def test_mlp_block_on_side_stream():
+    """The same chain with every call on a second stream (same default priority): the inputs
+    are produced on the current stream, the accumulators zero-filled there, and G_x is released
+    while up_proj's solve may still be queued.  The results equal the current-stream run bit
+    for bit (every kernel is deterministic)."""
+    torch = _torch()
+    say("mlp block on a side stream")
+    n, d, d_ff = 4096, 256, 512
+    spec = G.Spec.make(4, 128, False, 128, 0.01)
+    Wg = to_dev(synth.gen_weight(961, "g", d_ff, d, 0.02, "f16"))
+    Wu = to_dev(synth.gen_weight(961, "u", d_ff, d, 0.02, "f16"))
+    Wd = to_dev(synth.gen_weight(961, "dn", d, d_ff, 0.02, "f16"))
+    X = to_dev(synth.gen_acts(961, "x", n, d, "f16"))
+    a = BLK.quantize_mlp_block(Wg, Wu, Wd, X, spec)
+    side = torch.cuda.Stream()
+    b = BLK.quantize_mlp_block(Wg, Wu, Wd, X, spec, stream=side)
+    torch.cuda.synchronize()
+    for name in ("gate", "up", "down"):
+        for i in range(4):
+            assert torch.equal(a[name][i], b[name][i]), (name, i)
+    assert torch.equal(a["Y"], b["Y"]) and torch.equal(a["H_y"], b["H_y"])
+    for k in ("loss_gate", "loss_up", "loss_down"):
+        assert a[k] == b[k], k
