@@ -1,5 +1,6 @@
 """The decoder layer at LLaMA-7B shapes (d = 4096 in 32 heads of 128, d_ff = 11008,
-sequences of 2048 tokens; 16384 calibration tokens, so the products run in two chunks),
+sequences of 2048 tokens; 131072 calibration tokens, the token count of the 7B-layer
+workload, so the products run in sixteen chunks; INT3 asymmetric g128),
 through block.quantize_decoder_block as bench.py calls it, against what the oracle computes
 one entry at a time:
   * n1 and n2 on every token (rmsnorm of the GPU's own input), within one float16 step;
@@ -7,8 +8,9 @@ one entry at a time:
     before it in its sequence, from the GPU's n1 and packed q/k/v rows of that head, within
     the attention bound of the small-size tests;
   * h and Y on sampled tokens, from the GPU's O and n2 and packed layers;
-  * q_proj and o_proj on sampled rows: the oracle's column solve with the oracle's G of the
-    GPU's own calibration input (the tie-following comparison);
+  * q_proj, o_proj, gate_proj and down_proj on 64 sampled rows each: the oracle's column
+    solve with the oracle's own float64 H and G of the GPU's calibration input of that
+    sub-layer (the tie-following comparison);
   * down_proj (11008 columns): sum_q e_q^2 = Delta H_d Delta^T on sampled rows, and every
     weight on its group's grid.
 """
@@ -22,12 +24,12 @@ from post_weight_quantization_24_amd import gptq as G
 from post_weight_quantization_24_amd import synth
 from tests.parity import compare
 from tests.test_gpu_block import _mlp_tol, _step
-from tests.test_gpu_parity import _torch, codes_of, say
+from tests.test_gpu_parity import _torch, say
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
-D, D_FF, L, N_TOK = 4096, 11008, 2048, 16384
-BITS, GROUP, B, DAMP = 4, 128, 128, 0.01
+D, D_FF, L, N_TOK = 4096, 11008, 2048, 131072
+BITS, GROUP, B, DAMP = 3, 128, 128, 0.01
 
 
 def _rows(pack, r0, r1):
@@ -98,22 +100,27 @@ def test_decoder_block_7b_shapes():
     say("Y on %d sampled tokens: max err/tol %.3g" % (len(ts), float((err / tol).max())))
     assert np.all(err <= tol)
 
-    # column solves of q_proj and o_proj on sampled rows, on the GPU's own inputs
+    # column solves on sampled rows, on the GPU's own calibration inputs
     sd = dict(bits=BITS, group=GROUP, sym=False)
-    for nm, key in (("q_proj", "n1"), ("o_proj", "O")):
+    for nm, key in (("q_proj", "n1"), ("o_proj", "O"), ("gate_proj", "n2"), ("down_proj", "Y")):
         H = O.hessian(X[key])
-        Gx = O.prepare_g(H, DAMP)
-        sel = np.sort(rng.choice(D, 8, replace=False))
-        codes = codes_of(r[nm][0], BITS, D)[sel]
+        Hdamp, _ = O.damp(H, DAMP)
+        Gx = O.inv_chol_upper_reversed(Hdamp)
+        del Hdamp
+        d_row, d_col = shapes[nm]
+        sel = np.unique(np.concatenate([np.sort(rng.choice(d_row, 62, replace=False)),
+                                        [0, d_row - 1]]))
+        codes = O.unpack_codes(pk[nm][0][sel], BITS, d_col)
         st = compare(W[nm][sel], Gx, sd, codes, pk[nm][1][sel], pk[nm][2][sel], H=H, block=B)
         st.pop("fol")
-        say(nm, "sampled rows", st)
+        say(nm, "%d sampled rows" % sel.size, st)
+        del H, Gx
 
     # down_proj: sum of squared errors against Delta H_d Delta^T, grid membership
     Hy = r["H_y"].cpu().numpy().astype(np.float64)
     lam = DAMP * np.mean(np.diag(Hy))
     sel = np.sort(rng.choice(D, 6, replace=False))
-    codes = codes_of(r["down_proj"][0], BITS, D_FF)[sel]
+    codes = O.unpack_codes(pk["down_proj"][0][sel], BITS, D_FF)
     w_hat = O.dequantize(codes, pk["down_proj"][1][sel], pk["down_proj"][2][sel], GROUP)
     Dl = W["down_proj"][sel].astype(np.float64) - w_hat
     lhs = r["down_proj"][3].cpu().numpy()[sel]

@@ -1,21 +1,35 @@
-"""Full-size parity: the workloads at their real shapes, through the same calls and launch
-configuration as bench.py.
+"""Full-size parity: every layer, bit width and block size of the four large workloads at its
+real shape, through the same calls and launch configuration as bench.py, against the float64
+oracle on the same seeded inputs.
 
-q_proj layer (4096 x 4096, 262144 tokens, INT4 symmetric g128): the oracle runs end to end in
-float64 (its own Hessian over all tokens, its own G) and the column solve is compared on a
-sample of rows with the tie-following comparison (rows are independent given G).
+For each calibration input the oracle computes its own Hessian over all tokens (float64) and
+its own G (the reversed-Cholesky route, pinned against the literal route); the GPU computes
+its own H and G.  Then:
+  * H entry by entry: |H_gpu - H| / sqrt(H_ii H_jj) < 5e-5 (the float32 accumulation bound
+    of the small-size tests);
+  * G entry by entry against its row scale;
+  * every GPU column solve on sampled rows (rows are independent given G) with the
+    tie-following comparison: the oracle's column loop runs on the oracle's G, codes equal
+    except at positions within 1e-3 of a step of a rounding boundary (at most 0.1 % of them),
+    scales within 1e-5, zero points equal, the layer loss of the sampled rows within 0.5 %;
+    the sample holds the first and last row of at least eight 16-row workgroups of the
+    column-solve kernel, evenly spread rows and the last row;
+  * each sampled row's loss 1/2 D_r H D_r^T from the GPU's dequantization check (its own H)
+    within 0.5 % of the oracle's row loss (its own codes and H).  Where the GPU took the other
+    side of a near-tie (an equally correct result), the rest of that row's compensation takes
+    another path whose loss is as good but not the same number; such a row is compared with
+    the oracle that made the same choice at the tie (the followed run), every other row with
+    the oracle's own run.
 
-Larger layers (LLaMA-7B down_proj 4096 x 11008, 70B-shaped down_proj 8192 x 28672, the outlier
-layer at INT2 with B = 32), where a float64 Hessian over all tokens would take minutes on the
-host, are checked through what the oracle computes one entry at a time and through properties
-that hold at any size:
-  * sampled Hessian entries against float64 dot products of the inputs;
-  * the trailing 256 x 256 block of G against the oracle's factor of its own trailing Hessian
-    block (a trailing block of G depends only on the matching block of H_d) with lambda from
-    the oracle's own diagonal;
-  * G H_d G^T = I on sampled rows of G;
-  * every group on the grid (dequant check), and sum_q e_q^2 = Delta H_d Delta^T per row;
-  * the GPTQ layer loss below round-to-nearest on the same H.
+Workloads (page "大模型常见的量化方式", section on the layers of a large model, for the
+sub-layer shapes; page "量化", section GPTQ, for the method):
+  q_proj 4096 x 4096 over 262144 tokens, INT4 symmetric g128;
+  LLaMA-7B layer over 131072 tokens: q/k/v/gate/up on one input, o_proj and down_proj on
+    their own, INT4 and INT3 asymmetric g128;
+  70B-shaped MLP over 65536 tokens: gate/up (28672 x 8192) on one input, down (8192 x 28672)
+    on its own, INT4 asymmetric g128;
+  outlier layer 8192 x 8192 over 131072 tokens (1 % of channels x100), INT2 and INT3
+    asymmetric per channel, B in {32, 64, 128, 256}, one H and G for all eight runs.
 Each case prints its name before any GPU work.
 """
 
@@ -29,6 +43,8 @@ from tests.parity import compare
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
+ROWS_PER_WG = 16      # rows of one column-solve workgroup
+
 
 def _torch():
     import torch
@@ -40,128 +56,144 @@ def say(*a):
     print("[gpu-case]", *a, flush=True)
 
 
-def codes_of(qweight, bits, d_col):
-    return O.unpack_codes(qweight.cpu().numpy().view(np.uint32), bits, d_col)
+def sample_rows(d_row, n, n_wg=8):
+    """First and last row of n_wg evenly spread 16-row workgroups, the last row, and evenly
+    spread rows up to n in all."""
+    n_groups = (d_row + ROWS_PER_WG - 1) // ROWS_PER_WG
+    wgs = np.unique(np.linspace(0, n_groups - 1, n_wg).astype(int))
+    edge = np.concatenate([wgs * ROWS_PER_WG, np.minimum(wgs * ROWS_PER_WG + ROWS_PER_WG - 1,
+                                                         d_row - 1), [d_row - 1]])
+    rest = np.linspace(0, d_row - 1, max(n - edge.size, 0) + 2).astype(int)[1:-1]
+    return np.unique(np.concatenate([edge, rest]))
 
 
-def run_layer(wl, layer, bits, block):
-    """Generate the layer's inputs (kept on the host for the oracle) and run the three calls
-    as bench.py does: Hessian over all tokens, inverse factor, column solve, dequant check."""
+class _Inputs:
+    """The current calibration input: host X, the oracle's H and G, the GPU's H and G.
+    One input is kept at a time (the cases are ordered by input)."""
+    key = None
+    X = H = Gr = Hd = Gd = None
+
+
+_cur = _Inputs()
+
+
+def inputs(wl, xname):
     torch = _torch()
-    W = synth.layer_weight(wl, layer.name)
-    X = synth.layer_acts(wl, layer.x)
+    key = (wl.name, xname)
+    if _cur.key == key:
+        return _cur
+    _cur.key = None
+    _cur.X = _cur.H = _cur.Gr = _cur.Hd = _cur.Gd = None
+    torch.cuda.empty_cache()
+    d = wl.x_dim(xname)
+    say("input", wl.name, xname, wl.n_tok, d)
+    X = synth.layer_acts(wl, xname)
     dev = "cuda:0"
-    Wd = torch.from_numpy(W).to(dev)
     Xd = torch.from_numpy(X).to(dev)
-    d_col = layer.d_col
-    Hd = torch.zeros((d_col, d_col), dtype=torch.float32, device=dev)
+    Hd = torch.zeros((d, d), dtype=torch.float32, device=dev)
     G.hessian_accumulate(Hd, Xd)
     Gd = G.prepare_hinv(Hd, damp_frac=wl.damp, check=True)
-    spec = G.Spec.make(bits, wl.group, wl.sym, block, wl.damp)
-    qw, sc, ze, esq = G.quantize_layer(Wd, Gd, spec)
-    loss, row_loss, w_hat, off = G.dequant_check(qw, sc, ze, Wd, Hd, spec, want_w_hat=True)
     torch.cuda.synchronize()
     del Xd
-    return dict(W=W, X=X, Wd=Wd, Hd=Hd, Gd=Gd, spec=spec, qw=qw, sc=sc, ze=ze, esq=esq,
-                loss=loss, row_loss=row_loss, w_hat=w_hat, off=off)
-
-
-def test_fullsize_qproj_4096():
-    wl = synth.WORKLOADS["qproj_4096"]
-    layer = wl.layers[0]
-    say("full size", wl.name, layer.name, layer.d_row, layer.d_col, wl.n_tok)
-    r = run_layer(wl, layer, 4, 128)
-    d = layer.d_col
-    H = O.hessian(r["X"])                                   # float64 over all 262144 tokens
-    Hg = r["Hd"].cpu().numpy().astype(np.float64)
-    dg = np.sqrt(np.outer(np.diag(H), np.diag(H)))          # bounds sum_t |x_i x_j| (x2)
-    h_err = float((np.abs(Hg - H) / dg).max())
+    # float64 over all tokens: the sum over token ranges of the oracle's Hessian of each range
+    H = None
+    for t0 in range(0, X.shape[0], 16384):
+        part = O.hessian(X[t0:t0 + 16384])
+        H = part if H is None else H + part
+        del part
+        say("oracle H: tokens [0, %d)" % min(t0 + 16384, X.shape[0]))
+    Hdamp, _ = O.damp(H, wl.damp)
+    Gr = O.inv_chol_upper_reversed(Hdamp)
+    del Hdamp
+    say("oracle G done")
+    # H and G of the GPU against the oracle's
+    Hg = Hd.cpu().numpy()
+    dg = np.sqrt(np.diag(H))
+    h_err = 0.0
+    for r0 in range(0, d, 2048):
+        blk = np.abs(Hg[r0:r0 + 2048].astype(np.float64) - H[r0:r0 + 2048])
+        h_err = max(h_err, float((blk / dg[r0:r0 + 2048, None] / dg[None, :]).max()))
+    del Hg
     say("H max error / sqrt(H_ii H_jj)", h_err)
     assert h_err < 5e-5
-    Gr = O.prepare_g(H, wl.damp)
-    Gg = r["Gd"].cpu().numpy().astype(np.float64)
-    g_err = float((np.abs(Gg - Gr) / np.abs(Gr).max(axis=1, keepdims=True)).max())
+    Gg = Gd.cpu().numpy()
+    g_err = 0.0
+    for r0 in range(0, d, 2048):
+        ref = Gr[r0:r0 + 2048]
+        blk = np.abs(Gg[r0:r0 + 2048].astype(np.float64) - ref)
+        g_err = max(g_err, float((blk / np.abs(ref).max(axis=1, keepdims=True)).max()))
+    del Gg
     say("G max error / row scale", g_err)
     assert g_err < 2e-3
-    rows = np.linspace(0, layer.d_row - 1, 12).astype(int)
-    codes = codes_of(r["qw"], 4, d)
-    st = compare(r["W"][rows], Gr, dict(bits=4, group=wl.group, sym=wl.sym), codes[rows],
-                 r["sc"].cpu().numpy()[rows], r["ze"].cpu().numpy()[rows], H=H, block=128)
-    st.pop("fol")
-    say("column solve on rows", rows.tolist(), st)
-    assert r["off"].item() == 0
+    _cur.X, _cur.H, _cur.Gr, _cur.Hd, _cur.Gd, _cur.key = X, H, Gr, Hd, Gd, key
+    return _cur
 
 
-CASES = [("llama7b_layer", "down_proj", 4, 128), ("llama70b_mlp", "down_proj", 4, 128),
-         ("outlier_8192", "w", 2, 32)]
-
-
-@pytest.mark.parametrize("wl_name,layer_name,bits,block", CASES)
-def test_fullsize_large_layers(wl_name, layer_name, bits, block):
+def run_case(wl_name, layer_name, bits, block, n_rows):
     torch = _torch()
     wl = synth.WORKLOADS[wl_name]
     layer = wl.layer(layer_name)
-    say("full size", wl_name, layer_name, layer.d_row, layer.d_col, wl.n_tok, bits, block)
-    r = run_layer(wl, layer, bits, block)
-    X, d = r["X"], layer.d_col
-    Hg = r["Hd"].cpu().numpy()
-    rng = np.random.default_rng(5)
-
-    # sampled Hessian entries (and the whole diagonal) in float64
-    diag = np.empty(d)
-    for c0 in range(0, d, 2048):
-        xc = X[:, c0:c0 + 2048].astype(np.float64)
-        diag[c0:c0 + 2048] = 2.0 * np.einsum("ij,ij->j", xc, xc)
-    ii = np.concatenate([rng.integers(0, d, 48), d - 1 - np.arange(8)])
-    jj = np.concatenate([rng.integers(0, d, 48), d - 1 - np.arange(8)[::-1]])
-    ref = np.array([2.0 * np.dot(X[:, i].astype(np.float64), X[:, j].astype(np.float64))
-                    for i, j in zip(ii, jj)])
-    h_err = np.abs(Hg[ii, jj] - ref) / np.sqrt(diag[ii] * diag[jj])
-    assert np.abs(np.diag(Hg) - diag).max() / diag.max() < 5e-5
-    say("sampled H max error", float(h_err.max()))
-    assert h_err.max() < 5e-5
-
-    # trailing block of G from the oracle's own trailing Hessian block and diagonal
-    lam = wl.damp * diag.mean()
-    F = slice(d - 256, d)
-    XF = X[:, F].astype(np.float64)
-    HF = 2.0 * (XF.T @ XF) + lam * np.eye(256)
-    GF = O.inv_chol_upper(HF)
-    Gg = r["Gd"]
-    GgF = Gg[d - 256:, d - 256:].cpu().numpy().astype(np.float64)
-    g_err = float((np.abs(GgF - GF) / np.abs(GF).max(axis=1, keepdims=True)).max())
-    say("trailing G block max error / row scale", g_err)
-    assert g_err < 2e-3
-
-    # G H_d G^T = I on sampled rows (float64 on the device)
-    R = np.sort(rng.choice(d, 8, replace=False))
-    Hdd = r["Hd"].double()
-    lam_g = wl.damp * float(torch.diagonal(Hdd).mean())
-    Hdd.diagonal().add_(lam_g)
-    GR = Gg[R].double()
-    prod = (GR @ Hdd @ GR.T).cpu().numpy()
-    del Hdd
-    say("G H_d G^T on rows", R.tolist(), float(np.abs(prod - np.eye(len(R))).max()))
-    assert np.abs(prod - np.eye(len(R))).max() < 1e-3
-
-    # column solve: on the grid, the error identity, below round-to-nearest
-    assert r["off"].item() == 0
-    W = r["W"].astype(np.float64)
-    Wh = r["w_hat"].cpu().numpy().astype(np.float64)
-    Delta = W - Wh
-    esq = r["esq"].cpu().numpy()
-    ident = 2.0 * r["row_loss"].cpu().numpy() + lam_g * (Delta ** 2).sum(axis=1)
-    rel = np.abs(esq - ident) / ident
-    say("error identity max rel", float(rel.max()))
-    assert rel.max() < 1e-3
-    rtn = O.rtn_quantize(r["W"], bits, wl.group, wl.sym)
-    words = O.pack_codes(rtn["codes"], bits).view(np.int32)
-    spec = r["spec"]
-    rq = torch.from_numpy(words).to("cuda:0")
-    rs = torch.from_numpy(rtn["scales"].astype(np.float32)).to("cuda:0")
-    rz = torch.from_numpy(rtn["zeros"].astype(np.uint8)).to("cuda:0")
-    loss_rtn, _, _, off_rtn = G.dequant_check(rq, rs, rz, r["Wd"], r["Hd"], spec)
+    say("full size", wl_name, layer_name, layer.d_row, layer.d_col, wl.n_tok, "bits", bits,
+        "B", block)
+    inp = inputs(wl, layer.x)
+    W = synth.layer_weight(wl, layer.name)
+    Wd = torch.from_numpy(W).to("cuda:0")
+    spec = G.Spec.make(bits, wl.group, wl.sym, block, wl.damp)
+    qw, sc, ze, esq = G.quantize_layer(Wd, inp.Gd, spec)
+    loss, row_loss, _, off = G.dequant_check(qw, sc, ze, Wd, inp.Hd, spec)
     torch.cuda.synchronize()
-    say("loss gptq %.6g rtn %.6g" % (r["loss"].item(), loss_rtn.item()))
-    assert off_rtn.item() == 0
-    assert r["loss"].item() < loss_rtn.item()
+    assert off.item() == 0
+    rows = sample_rows(layer.d_row, n_rows)
+    words = qw.cpu().numpy().view(np.uint32)[rows]
+    codes = O.unpack_codes(words, bits, layer.d_col)
+    sd = dict(bits=bits, group=wl.group, sym=wl.sym)
+    ref = O.gptq_quantize(W[rows], inp.Gr, bits, wl.group, wl.sym, block=block)
+    st = compare(W[rows], inp.Gr, sd, codes, sc.cpu().numpy()[rows], ze.cpu().numpy()[rows],
+                 H=inp.H, block=block, unfollowed=ref)
+    fol = st.pop("fol")
+    # per-row losses: the GPU's check (its own H) against the oracle's (its own codes and H)
+    def row_losses(w_hat):
+        D = W[rows].astype(np.float64) - w_hat
+        return 0.5 * np.sum((D @ inp.H) * D, axis=1)
+
+    own, followed = row_losses(ref["w_hat"]), row_losses(fol["w_hat"])
+    gpu_rows = row_loss.cpu().numpy()[rows]
+    tie_rows = np.any(fol["codes"] != ref["codes"], axis=1)
+    rel_own = np.abs(gpu_rows - own) / own
+    rel = np.where(tie_rows, np.abs(gpu_rows - followed) / followed, rel_own)
+    say("rows", rows.size, "raw agree %.6f, ties followed %d (%.2e), scale rel %.2e, loss rel %.2e"
+        % (st["raw_agree"], st["ties_followed"], st["tie_frac"], st["scale_rel"], st["loss_rel"]))
+    say("row loss rel: max %.2e (%d rows with a followed tie, against the followed run; %.2e "
+        "against the oracle's own run)" % (float(rel.max()), int(tie_rows.sum()),
+                                           float(rel_own.max())))
+    assert rel.max() <= 5e-3, (rows[np.argmax(rel)], float(rel.max()))
+    whole = float(loss.item())
+    say("layer loss (GPU check, all rows) %.6g" % whole)
+    assert np.isfinite(whole) and whole > 0
+    del Wd, qw, sc, ze, esq, row_loss, loss
+
+
+CASES = [("qproj_4096", "q_proj", 4, 128, 256)]
+for _bits in (4, 3):
+    CASES += [("llama7b_layer", nm, _bits, 128, 96)
+              for nm in ("q_proj", "k_proj", "v_proj", "gate_proj", "up_proj")]
+for _bits in (4, 3):
+    CASES += [("llama7b_layer", "o_proj", _bits, 128, 96)]
+for _bits in (4, 3):
+    CASES += [("llama7b_layer", "down_proj", _bits, 128, 96)]
+CASES += [("llama70b_mlp", "gate_proj", 4, 128, 96), ("llama70b_mlp", "up_proj", 4, 128, 96),
+          ("llama70b_mlp", "down_proj", 4, 128, 96)]
+CASES += [("outlier_8192", "w", _bits, _b, 96) for _bits in (2, 3) for _b in (32, 64, 128, 256)]
+
+
+@pytest.mark.parametrize("wl_name,layer_name,bits,block,n_rows", CASES,
+                         ids=["%s-%s-int%d-B%d" % c[:4] for c in CASES])
+def test_fullsize(wl_name, layer_name, bits, block, n_rows):
+    run_case(wl_name, layer_name, bits, block, n_rows)
+
+
+def test_fullsize_release():
+    """Drops the last input kept between the cases above (host and device memory)."""
+    _cur.key = None
+    _cur.X = _cur.H = _cur.Gr = _cur.Hd = _cur.Gd = None
+    _torch().cuda.empty_cache()
