@@ -184,16 +184,22 @@ int gptq_dequant_matvec(const uint32_t* qweight, const float* scales, const uint
  * matrix cores (page "量化", section AWQ: W4A16, INT4 weights with fp16 activations; section
  * GPTQ: the quantized layer's output).  Group by group:
  *     y[i][r] = sum_g s[r][g] * sum_{c in group g} x[i][c] * (code[r][c] - z[r][g]),
- * fp16 x times the exact integers code - z in fp32 sums, scaled and added in fp32.  The codes
- * are first expanded into the workspace as fp16 integers (d_row x d_col halfs), so the call
- * pays off from a few hundred activation rows on; gptq_dequant_matvec is the small-n path.
+ * fp16 x times the exact integers code - z in fp32 sums, scaled and added in fp32.  When d_col
+ * and the group size are multiples of 64 (per-channel: d_col a multiple of 64), the codes are
+ * read packed and expanded in the product's main loop (page "量化", section AWQ: the
+ * weight-only kernel dequantizes inside the GEMM loop), so the weights cross HBM at b bits
+ * each and no workspace is used; other layouts (groups of 16 or 32) expand the codes into
+ * the workspace as fp16 integers (d_row x d_col halfs) first.  The call pays off from a few
+ * hundred activation rows on; gptq_dequant_matvec is the small-n path.
  *   qweight, scales, zeros  as gptq_quantize_layer writes them; d_col a multiple of 32;
  *            bits 2, 3, 4 or 8; group 0 or a multiple of 16 dividing d_col.
- *   x  [n x d_col] fp16, row stride ldx >= d_col, a multiple of 8, x 16-byte aligned; n >= 0.
+ *   x  [n x d_col] fp16, row stride d_col <= ldx <= 2^22, a multiple of 8, x 16-byte aligned;
+ *      n >= 0.
  *   y  [n x d_row] float32 output, row stride ldy >= d_row (overwritten).
- *   Workspace: gptq_dequant_matmul_workspace_size(d_row, d_col) bytes, 256-byte aligned.
+ *   Workspace: gptq_dequant_matmul_workspace_size(d_row, d_col, bits, group) bytes, 256-byte
+ *      aligned; 0 (ws may be NULL) for the layouts read packed.
  * Errors: GPTQ_EINVAL, GPTQ_ENOWS, GPTQ_EHIP. */
-size_t gptq_dequant_matmul_workspace_size(int64_t d_row, int64_t d_col);
+size_t gptq_dequant_matmul_workspace_size(int64_t d_row, int64_t d_col, int bits, int group);
 int gptq_dequant_matmul(const uint32_t* qweight, const float* scales, const uint8_t* zeros,
                         int64_t d_row, int64_t d_col, int bits, int group, const void* x, int64_t n,
                         int64_t ldx, float* y, int64_t ldy, void* ws, size_t ws_bytes,

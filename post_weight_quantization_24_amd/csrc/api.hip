@@ -304,9 +304,11 @@ int gptq_dequant_matvec(const uint32_t* qweight, const float* scales, const uint
   return GPTQ_OK;
 }
 
-size_t gptq_dequant_matmul_workspace_size(int64_t d_row, int64_t d_col) {
+size_t gptq_dequant_matmul_workspace_size(int64_t d_row, int64_t d_col, int bits, int group) {
   if (d_row < 1 || d_col < 32 || d_col % 32 != 0 || d_row > (int64_t)1 << 30 || d_col > (int64_t)1 << 20)
     return 0;
+  const int64_t g = group == 0 ? d_col : group;
+  if (gptq::qgemm_packed_ok(d_col, bits, g, d_col)) return 0;   // codes read in the main loop
   return gptq::align_up((size_t)d_row * d_col * sizeof(_Float16), 256);
 }
 
@@ -319,15 +321,23 @@ int gptq_dequant_matmul(const uint32_t* qweight, const float* scales, const uint
   if ((rc = check_layer(GPTQ_F16, d_row, d_col)) != GPTQ_OK) return rc;
   if ((rc = check_packed(bits, group, d_col)) != GPTQ_OK) return rc;
   if (n < 0) return fail(GPTQ_EINVAL, "n < 0");
-  if (ldx < d_col || ldx % 8 != 0 || ldy < d_row)
-    return fail(GPTQ_EINVAL, "ldx >= d_col (a multiple of 8) and ldy >= d_row required");
+  if (ldx < d_col || ldx % 8 != 0 || ldy < d_row || ldx > (int64_t)1 << 22)
+    return fail(GPTQ_EINVAL, "d_col <= ldx <= 2^22 (a multiple of 8) and ldy >= d_row required");
   if (n == 0) return GPTQ_OK;
   if (!qweight || !scales || !zeros || !x || !y)
     return fail(GPTQ_EINVAL, "qweight, scales, zeros, x and y must not be NULL");
   if (!aligned(x, 16)) return fail(GPTQ_EINVAL, "x must be 16-byte aligned");
-  const size_t need = gptq_dequant_matmul_workspace_size(d_row, d_col);
-  if (!ws || ws_bytes < need) return fail(GPTQ_ENOWS, "workspace of %zu bytes needed", need);
-  if (!aligned(ws, 256)) return fail(GPTQ_EINVAL, "workspace must be 256-byte aligned");
+  const size_t need = gptq_dequant_matmul_workspace_size(d_row, d_col, bits, group);
+  if (need && (!ws || ws_bytes < need)) return fail(GPTQ_ENOWS, "workspace of %zu bytes needed", need);
+  if (need && !aligned(ws, 256)) return fail(GPTQ_EINVAL, "workspace must be 256-byte aligned");
+  if (!need) {
+    const int64_t g = group == 0 ? d_col : group;
+    hipError_t e = gptq::qgemm_packed_f16(static_cast<const _Float16*>(x), ldx, n, qweight, zeros,
+                                          scales, d_row, d_col, bits, g, y, ldy,
+                                          static_cast<hipStream_t>(stream), "dequant_matmul");
+    if (e != hipSuccess) return hip_fail(e, "gptq_dequant_matmul");
+    return GPTQ_OK;
+  }
   const int64_t g = group == 0 ? d_col : group;
   hipStream_t s = static_cast<hipStream_t>(stream);
   _Float16* B = static_cast<_Float16*>(ws);

@@ -109,6 +109,13 @@ hipError_t mlp_launch(const void* X, int64_t n_tok, int64_t d, int64_t ldx,
 // matrix cores (A fp16 [M x K], rows 16-byte aligned; S the scales [N x K/g]; C fp32).
 void expand_codes_f16(const uint32_t* q, const uint8_t* z, int64_t N, int64_t K, int bits,
                       int64_t g, _Float16* B, hipStream_t s);
+// Product of fp16 A [M x K] with a packed layer [N x K] (codes, zeros, scales), dequantized
+// inside the main loop; for bits 2/3/4/8, K and g multiples of 64 (qgemm_packed_ok).
+bool qgemm_packed_ok(int64_t K, int bits, int64_t g, int64_t lda);
+hipError_t qgemm_packed_f16(const _Float16* A, int64_t lda, int64_t M, const uint32_t* q,
+                            const uint8_t* z, const float* S, int64_t N, int64_t K, int bits,
+                            int64_t g, float* C, int64_t ldc, hipStream_t s,
+                            const char* prof_name);
 hipError_t qgemm_f16(const _Float16* A, int64_t lda, int64_t M, const _Float16* B, int64_t N,
                      int64_t K, const float* S, int64_t g, float* C, int64_t ldc, hipStream_t s,
                      const char* prof_name);

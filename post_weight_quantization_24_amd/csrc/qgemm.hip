@@ -17,6 +17,8 @@
 // into registers while the current one is multiplied).  Rows of a stage are padded to 72
 // halfs so the eight lanes that a 16-byte LDS read serves at once fall in distinct banks.
 
+#include <type_traits>
+
 #include "gptq_internal.h"
 
 namespace gptq {
@@ -357,7 +359,317 @@ qgemm_dma(const _Float16* __restrict__ A, int64_t lda, int64_t M, const _Float16
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// The same product straight from the packed codes: dequantization inside the main loop (page
+// "量化", section AWQ: the weight-only kernel unpacks the codes in the GEMM's main loop, so the
+// weights cross HBM at b bits each).  Tiles, waves and the ring of three K stages are those
+// of qgemm_dma; a stage holds 128 rows of A (fp16, 16-byte copies) and the 256 rows of packed
+// codes of its 64 columns (8 b bytes per row, dword copies), so a stage of a 4-bit layer is
+// 24 KB instead of 48 KB.
+//
+// K order inside a stage: lane half h of an MFMA fragment (lanes 32 h .. 32 h + 31) takes the
+// stage's columns 32 h .. 32 h + 31 and step kk (0..3) the eight columns 32 h + 8 kk .. + 7.
+// The sum over a stage's 64 columns does not depend on which MFMA step and lane half a column
+// goes to, as long as A and B agree; with this order each lane's 32 codes of the stage are
+// contiguous (4 b bytes, one 16-byte LDS read for 4-bit codes) and are expanded in registers,
+// 8 per step: 1024 + c is the fp16 with bits 0x6400 | c, and one packed fp16 add of
+// -(1024 + z) gives c - z exactly.  Groups are whole stages (g % 64 == 0).
+//
+// LDS layout of the codes: row r's dwords of the stage at r * 2 b .. + 2 b - 1; for 4-bit codes
+// the two 16-byte halves of a row swap places in rows with bit 3 set, so the 16 lanes that one
+// LDS read cycle serves (rows r .. r + 15, the same half) fall in distinct banks.
+
+template <int BITS>
+struct PackedCfg {
+  static constexpr int RD = 2 * BITS;                    // dwords per row and stage
+  static constexpr int B_BYTES = DN * RD * 4;
+  static constexpr int STAGE = DA_BYTES + B_BYTES;
+  static constexpr int A_CPW = DA_BYTES / 1024 / DWAVES;   // 1 KB copies of A per wave: 2
+  static constexpr int B_CPW = DN * RD / 64 / DWAVES;      // 256 B copies of B per wave: BITS
+  static constexpr int CPW = A_CPW + B_CPW;
+  static constexpr int CHUNK = BITS;                      // dwords of codes per lane and stage
+};
+
+// LDS dword position of global dword j of row r's stage segment (an involution)
+template <int BITS>
+__device__ __forceinline__ int pk_pos(int row, int j) {
+  if constexpr (BITS == 4) return j ^ (((row >> 3) & 1) << 2);
+  return j;
+}
+
+// One wave-wide copy of 64 dwords global -> LDS: lane l's dword at buffer offset voff lands at
+// lds_base + 4 l.
+__device__ __forceinline__ void dcopy4(rsrc_t rsrc, uint32_t lds_base, int voff) {
+  __asm__ volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                   :
+                   : "v"(voff), "s"(rsrc), "s"(lds_base)
+                   : "memory", "m0");
+}
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_pair(uint32_t lo, uint32_t hi) {
+  return lo | (hi << 16) | 0x64006400u;
+}
+
+// (w & mask) | magic in one v_and_or_b32 (gfx9 VOP3 takes no literal: the mask comes from an
+// SGPR, the magic from a VGPR).
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  __asm__("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(magic));
+  return r;
+}
+
+__device__ __forceinline__ half2v as_h2(uint32_t u) {
+  half2v h;
+  __builtin_memcpy(&h, &u, 4);
+  return h;
+}
+
+// Eight codes of step kk from the lane's chunk as fp16 (c - z), in the slot order of
+// pk_slot_order: 4-bit codes come out as (c0, c4), (c1, c5), (c2, c6), (c3, c7) (a nibble and
+// the one four places up share the halves of a dword: (w & 0x000F000F) | 0x64006400 is the
+// pair 1024 + c; the odd nibbles sit 4 bits higher, 1024 + 16 c, and one packed FMA by 1/16
+// brings them back), other widths in natural order.  Every value is a small integer, exact in
+// fp16, and so is every step.
+template <int BITS>
+__device__ __forceinline__ half8 pk_expand(const uint32_t* ch, int kk, half2v nz, half2v nz16) {
+  half2v h[4];
+  if constexpr (BITS == 4) {
+    const uint32_t w = ch[kk], w8 = w >> 8;
+    const uint32_t magic = __builtin_amdgcn_readfirstlane(0x64006400u);
+    const half2v sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    h[0] = as_h2(and_or(w, 0x000F000Fu, magic)) + nz;
+    h[1] = as_h2(and_or(w, 0x00F000F0u, magic)) * sixteenth + nz16;
+    h[2] = as_h2(and_or(w8, 0x000F000Fu, magic)) + nz;
+    h[3] = as_h2(and_or(w8, 0x00F000F0u, magic)) * sixteenth + nz16;
+  } else if constexpr (BITS == 8) {
+    const uint32_t w0 = ch[2 * kk], w1 = ch[2 * kk + 1];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {  // bytes 2p, 2p + 1 of (w1:w0), each widened to a half
+      const uint32_t sel = (2u * p) | (0x0Cu << 8) | ((2u * p + 1u) << 16) | (0x0Cu << 24);
+      h[p] = as_h2(__builtin_amdgcn_perm(w1, w0, sel) | 0x64006400u) + nz;
+    }
+  } else {
+    // window of the step's 8 BITS bits, from bit 8 BITS kk of the chunk
+    constexpr int W = 8 * BITS;
+    const int bit = W * kk, i = bit >> 5, sh = bit & 31;
+    const uint32_t lo = ch[i];
+    const uint32_t hi = (i + 1 < BITS) ? ch[i + 1] : 0u;
+    const uint32_t win = sh ? __builtin_amdgcn_alignbit(hi, lo, (uint32_t)sh) : lo;
+    constexpr uint32_t M = (1u << BITS) - 1u;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      h[p] = as_h2(pk_pair((win >> (BITS * 2 * p)) & M, (win >> (BITS * (2 * p + 1))) & M)) + nz;
+  }
+  half8 out;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    out[2 * p] = h[p][0];
+    out[2 * p + 1] = h[p][1];
+  }
+  return out;
+}
+
+// A's eight fp16 of one fragment, in the slot order of the B expansion: for 4-bit codes
+// (a0, a4, a1, a5, a2, a6, a3, a7), else unchanged.
+template <int BITS>
+__device__ __forceinline__ half8 pk_slot_order(half8 a) {
+  if constexpr (BITS == 4) {
+    uint32_t d[4], o[4];
+    __builtin_memcpy(d, &a, 16);
+    o[0] = __builtin_amdgcn_perm(d[2], d[0], 0x05040100u);   // a0, a4
+    o[1] = __builtin_amdgcn_perm(d[2], d[0], 0x07060302u);   // a1, a5
+    o[2] = __builtin_amdgcn_perm(d[3], d[1], 0x05040100u);   // a2, a6
+    o[3] = __builtin_amdgcn_perm(d[3], d[1], 0x07060302u);   // a3, a7
+    half8 r;
+    __builtin_memcpy(&r, o, 16);
+    return r;
+  } else {
+    return a;
+  }
+}
+
+template <int BITS>
+__global__ void __launch_bounds__(64 * DWAVES, 1)
+qgemm_packed(const _Float16* __restrict__ A, int64_t lda, int64_t M,
+             const uint32_t* __restrict__ Q, const uint8_t* __restrict__ Z, int64_t N, int64_t K,
+             const float* __restrict__ S, int64_t n_groups, int spg, float* __restrict__ C,
+             int64_t ldc) {
+  using P = PackedCfg<BITS>;
+  __shared__ __attribute__((aligned(16))) char lds[DNST * P::STAGE];
+  const int64_t tiles_m = (M + DM - 1) / DM;
+  const int64_t tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+  const int64_t m0 = tm * DM, n0 = tn * DN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int li = lane & 31, lh = lane >> 5;
+  const int64_t wpr = K * BITS / 32;                     // words per row of codes
+  const int64_t rows_a = M - m0 < DM ? M - m0 : DM;
+  const int64_t rows_b = N - n0 < DN ? N - n0 : DN;
+  const rsrc_t ra = make_rsrc(A + m0 * lda, rows_a * lda * 2);
+  const rsrc_t rb = make_rsrc(Q + n0 * wpr, rows_b * wpr * 4);
+  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)lds);
+
+  // copies of stage st: A copy q (< 16) covers rows 8 q .. 8 q + 7; B copy q covers the
+  // stage's LDS dwords 64 q .. 64 q + 63 of the code block
+  auto issue = [&](int st, int slot) {
+    const uint32_t sbase = lds0 + (uint32_t)(slot * P::STAGE);
+#pragma unroll
+    for (int c = 0; c < P::A_CPW; ++c) {
+      const int q = wave * P::A_CPW + c;
+      const int row = 8 * q + (lane >> 3);
+      const int voff = (int)((row * lda + st * DK + 8 * dswz(row, lane & 7)) * 2);
+      dcopy(ra, sbase + (uint32_t)q * 1024u, voff);
+    }
+#pragma unroll
+    for (int c = 0; c < P::B_CPW; ++c) {
+      const int q = wave * P::B_CPW + c;
+      const int L = 64 * q + lane;
+      const int row = L / P::RD, jl = L % P::RD;
+      const int voff = (int)((row * wpr + st * P::RD + pk_pos<BITS>(row, jl)) * 4);
+      dcopy4(rb, sbase + (uint32_t)DA_BYTES + (uint32_t)q * 256u, voff);
+    }
+  };
+
+  floatx16 acc[2][2], part[2][2];
+  const floatx16 zero16 = {};
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = part[a][b] = zero16;
+  const int64_t col0 = n0 + wn * 64 + li, col1 = col0 + 32;
+  const int64_t c0 = (col0 < N ? col0 : N - 1) * n_groups, c1 = (col1 < N ? col1 : N - 1) * n_groups;
+  float sc0 = S[c0], sc1 = S[c1];
+  // -(1024 + z) and -(64 + z) for the two B rows of this lane, per group
+  half2v nz[2], nz16[2];
+  auto zero_points = [&](int64_t gi) {
+    const float z0 = (float)Z[c0 + gi], z1 = (float)Z[c1 + gi];
+    const _Float16 a0 = (_Float16)(-1024.0f - z0), a1 = (_Float16)(-1024.0f - z1);
+    const _Float16 b0 = (_Float16)(-64.0f - z0), b1 = (_Float16)(-64.0f - z1);
+    nz[0] = half2v{a0, a0};
+    nz[1] = half2v{a1, a1};
+    nz16[0] = half2v{b0, b0};
+    nz16[1] = half2v{b1, b1};
+  };
+  zero_points(0);
+  int64_t grp = 0;
+
+  const int nst = (int)(K / DK);
+  issue(0, 0);
+  if (nst > 1) issue(1, 1);
+  int slot = 0, gstep = 0;          // ring slot of stage st, stage index within its group
+  for (int st = 0; st < nst; ++st) {
+    if (st + 1 < nst) dwait_vmcnt<P::CPW>();
+    else dwait_vmcnt<0>();
+    dbarrier();
+    if (st + 2 < nst) issue(st + 2, slot == 0 ? 2 : slot - 1);
+    const char* sb = lds + slot * P::STAGE;
+    const bool fresh = gstep == 0;
+    // this lane's codes of the stage for its two B rows
+    uint32_t ch[2][P::CHUNK];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int row = wn * 64 + b * 32 + li;
+      const uint32_t* rb_l = reinterpret_cast<const uint32_t*>(sb + DA_BYTES) + row * P::RD;
+      if constexpr (BITS == 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(rb_l + pk_pos<4>(row, 4 * lh));
+        ch[b][0] = v.x; ch[b][1] = v.y; ch[b][2] = v.z; ch[b][3] = v.w;
+      } else if constexpr (BITS == 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(rb_l + 8 * lh);
+        const uint4 u = *reinterpret_cast<const uint4*>(rb_l + 8 * lh + 4);
+        ch[b][0] = v.x; ch[b][1] = v.y; ch[b][2] = v.z; ch[b][3] = v.w;
+        ch[b][4] = u.x; ch[b][5] = u.y; ch[b][6] = u.z; ch[b][7] = u.w;
+      } else if constexpr (BITS == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(rb_l + 2 * lh);
+        ch[b][0] = v.x; ch[b][1] = v.y;
+      } else {
+#pragma unroll
+        for (int j = 0; j < BITS; ++j) ch[b][j] = rb_l[BITS * lh + j];
+      }
+    }
+    auto step = [&](int kk, auto first) {
+      const int lslot = 4 * lh + kk;
+      half8 af[2], bf[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const int row = wm * 64 + a * 32 + li;
+        af[a] = pk_slot_order<BITS>(
+            *reinterpret_cast<const half8*>(sb + row * DROW + 16 * dswz(row, lslot)));
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) bf[b] = pk_expand<BITS>(ch[b], kk, nz[b], nz16[b]);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          part[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              af[a], bf[b], decltype(first)::value ? zero16 : part[a][b], 0, 0, 0);
+    };
+    if (fresh) step(0, std::true_type{});
+    else step(0, std::false_type{});
+#pragma unroll
+    for (int kk = 1; kk < DK / 16; ++kk) step(kk, std::false_type{});
+    slot = slot == DNST - 1 ? 0 : slot + 1;
+    if (++gstep == spg) {                  // the group ends with this stage
+      gstep = 0;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          acc[a][0][c] += sc0 * part[a][0][c];
+          acc[a][1][c] += sc1 * part[a][1][c];
+        }
+      ++grp;
+      if (grp < n_groups) {
+        sc0 = S[c0 + grp];
+        sc1 = S[c1 + grp];
+        zero_points(grp);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t col = n0 + wn * 64 + b * 32 + li;
+      if (col >= N) continue;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const int64_t row = m0 + wm * 64 + a * 32 + 8 * (c >> 2) + 4 * lh + (c & 3);
+        if (row < M) C[row * ldc + col] = acc[a][b][c];
+      }
+    }
+}
+
 }  // namespace
+
+bool qgemm_packed_ok(int64_t K, int bits, int64_t g, int64_t lda) {
+  return (bits == 2 || bits == 3 || bits == 4 || bits == 8) && K % DK == 0 && g % DK == 0 &&
+         (int64_t)DM * lda * 2 < ((int64_t)1 << 31) &&
+         (int64_t)DN * (K * bits / 8) < ((int64_t)1 << 31);
+}
+
+hipError_t qgemm_packed_f16(const _Float16* A, int64_t lda, int64_t M, const uint32_t* q,
+                            const uint8_t* z, const float* S, int64_t N, int64_t K, int bits,
+                            int64_t g, float* C, int64_t ldc, hipStream_t s,
+                            const char* prof_name) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (!qgemm_packed_ok(K, bits, g, lda)) return hipErrorInvalidValue;
+  ProfScope ps(prof_name, s);
+  const int64_t tiles = ceil_div(M, DM) * ceil_div(N, DN);
+  const dim3 grid((unsigned)tiles), block(64 * DWAVES);
+  const int spg = (int)(g / DK);
+  switch (bits) {
+    case 2: hipLaunchKernelGGL(qgemm_packed<2>, grid, block, 0, s, A, lda, M, q, z, N, K, S, K / g, spg, C, ldc); break;
+    case 3: hipLaunchKernelGGL(qgemm_packed<3>, grid, block, 0, s, A, lda, M, q, z, N, K, S, K / g, spg, C, ldc); break;
+    case 4: hipLaunchKernelGGL(qgemm_packed<4>, grid, block, 0, s, A, lda, M, q, z, N, K, S, K / g, spg, C, ldc); break;
+    default: hipLaunchKernelGGL(qgemm_packed<8>, grid, block, 0, s, A, lda, M, q, z, N, K, S, K / g, spg, C, ldc); break;
+  }
+  return hipGetLastError();
+}
 
 void expand_codes_f16(const uint32_t* q, const uint8_t* z, int64_t N, int64_t K, int bits,
                       int64_t g, _Float16* B, hipStream_t s) {

@@ -55,12 +55,11 @@ _SIGS = {
                             _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "gptq_dequant_matvec": ([_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _int, _i64, _i64, _vp,
                              _i64, _vp], _int),
-    "gptq_dequant_matmul_workspace_size": ([_i64, _i64], _sz),
+    "gptq_dequant_matmul_workspace_size": ([_i64, _i64, _int, _int], _sz),
     "gptq_dequant_matmul": ([_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64,
                              _vp, _sz, _vp], _int),
     "gptq_act_absmean_workspace_size": ([_i64, _i64], _sz),
     "gptq_act_absmean": ([_vp, _i64, _vp, _int, _i64, _i64, _vp, _sz, _vp], _int),
-    "gptq_act_absmean_noalloc": ([_vp, _i64, _vp, _int, _i64, _i64, _vp], _int),
     "gptq_awq_workspace_size": ([_i64, _i64], _sz),
     "gptq_awq_search": ([_vp, _int, _i64, _i64, _vp, _vp, _i64, ctypes.POINTER(Spec), _int, _vp,
                          _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
@@ -295,17 +294,6 @@ def act_absmean(sx_sum, X, ws=None, stream=None):
 
 
 @_streamed
-def act_absmean_noalloc(sx_sum, X, stream=None):
-    """sx_sum [d] float64 += sum over the rows of X of |x|, with the library's own scratch
-    (gptq_act_absmean_noalloc: no workspace, nothing allocated)."""
-    d = sx_sum.shape[0]
-    assert X.dim() == 2 and X.shape[1] == d and X.stride(1) == 1 and sx_sum.is_contiguous()
-    _check(lib().gptq_act_absmean_noalloc(sx_sum.data_ptr(), d, X.data_ptr(), _dtype_code(X),
-                                          X.shape[0], X.stride(0), _stream_handle(stream)))
-    return sx_sum
-
-
-@_streamed
 def awq_search(W, H, sx_sum, n_tok: int, spec: Spec, n_grid: int = 20, ws=None, stream=None):
     """Returns (qweight, scales, zeros, s [d_col] float32, losses [n_grid] float64,
     best int32[1]) of gptq_awq_search."""
@@ -359,10 +347,12 @@ def dequant_matmul(qweight, scales, zeros, x, bits: int, group: int, d_col: int,
     assert x.dtype == torch.float16 and x.stride(1) == 1 and x.shape[1] == d_col
     if y is None:
         y = torch.empty((n, d_row), dtype=torch.float32, device=x.device)
-    ws = _workspace(lib().gptq_dequant_matmul_workspace_size(d_row, d_col), x.device, ws)
+    need = lib().gptq_dequant_matmul_workspace_size(d_row, d_col, bits, group)
+    ws = _workspace(need, x.device, ws) if need else ws
     _check(lib().gptq_dequant_matmul(qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), d_row,
                                      d_col, bits, group, x.data_ptr(), n, x.stride(0), y.data_ptr(),
-                                     y.stride(0), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                     y.stride(0), ws.data_ptr() if ws is not None else None,
+                                     ws.numel() * ws.element_size() if ws is not None else 0,
                                      _stream_handle(stream)))
     return y
 

@@ -270,11 +270,16 @@ def test_attention_half_validation(lib):
 
 def test_dequant_matmul_validation(lib):
     f = lib.gptq_dequant_matmul
-    ws = lib.gptq_dequant_matmul_workspace_size(512, 1024)
-    assert ws >= 512 * 1024 * 2                    # the codes as fp16 integers
-    assert lib.gptq_dequant_matmul_workspace_size(512, 1000) == 0
+    ws = lib.gptq_dequant_matmul_workspace_size(512, 1024, 4, 32)
+    assert ws >= 512 * 1024 * 2                    # groups of 32: the codes as fp16 integers
+    assert lib.gptq_dequant_matmul_workspace_size(512, 1000, 4, 0) == 0
+    # groups that are whole 64-column stages are read packed: no workspace
+    for bits in (2, 3, 4, 8):
+        for group in (0, 64, 128, 256):
+            assert lib.gptq_dequant_matmul_workspace_size(512, 1024, bits, group) == 0
+    assert lib.gptq_dequant_matmul_workspace_size(512, 1056, 4, 0) > 0     # d_col % 64 != 0
 
-    def call(n=100, d_row=512, d_col=1024, bits=4, group=128, ldx=1024, ldy=512, wsz=ws, x=FAKE):
+    def call(n=100, d_row=512, d_col=1024, bits=4, group=32, ldx=1024, ldy=512, wsz=ws, x=FAKE):
         return f(FAKE, FAKE, FAKE, d_row, d_col, bits, group, x, n, ldx, FAKE, ldy, FAKE, wsz, None)
 
     assert call(bits=6) == G.EINVAL
@@ -285,4 +290,6 @@ def test_dequant_matmul_validation(lib):
     assert call(x=ctypes.c_void_p(0x10008)) == G.EINVAL
     assert call(n=-1) == G.EINVAL
     assert call(wsz=ws - 1) == G.ENOWS
+    assert call(ldx=(1 << 22) + 8) == G.EINVAL
     assert call(n=0) == G.OK
+

@@ -25,6 +25,9 @@ pytestmark = pytest.mark.gpu
     (5000, 640, 1024, 2, 16),     # one-MFMA groups
     (77, 96, 8192, 8, 0),         # per-channel, fewer outputs than a tile
     (130, 200, 96, 4, 32),        # d_col with a half K stage
+    (2500, 300, 2048, 2, 128),    # INT2 read packed, ragged tiles both ways
+    (129, 257, 640, 4, 0),        # per-channel INT4 read packed, one row past a tile each way
+    (64, 512, 1024, 8, 256),      # INT8 read packed, groups of four stages
 ])
 def test_dequant_matmul(n, d_row, d_col, bits, group):
     torch = _torch()
@@ -103,3 +106,24 @@ def test_dequant_matmul_70b_shape_sampled():
         worst = max(worst, abs(float(v) - ref) / tol)
         assert abs(float(v) - ref) <= tol, (t, r)
     say("max err / tol over 64 samples %.3g" % worst)
+
+
+def test_dequant_matmul_strided_x():
+    """x with a row stride above d_col (a column slice of a wider activation buffer), on the
+    packed path; the product equals the one on a contiguous copy bit for bit."""
+    torch = _torch()
+    say("dequant_matmul strided x")
+    rng = np.random.default_rng(1031)
+    d_row, d_col, bits, group, n = 700, 1024, 4, 128, 333
+    words, scales, zeros = packed_layer(rng, d_row, d_col, bits, group)
+    dev = "cuda:0"
+    q = torch.from_numpy(words.view(np.int32)).to(dev)
+    s = torch.from_numpy(scales).to(dev)
+    z = torch.from_numpy(zeros).to(dev)
+    wide = torch.from_numpy(acts(rng, n, d_col + 64)).to(dev)
+    xs = wide[:, 32:32 + d_col]
+    assert xs.stride(0) == d_col + 64
+    a = G.dequant_matmul(q, s, z, xs, bits, group, d_col)
+    b = G.dequant_matmul(q, s, z, xs.contiguous(), bits, group, d_col)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
