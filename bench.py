@@ -51,6 +51,8 @@ def parse():
                    help="skip the AWQ scale-search leg after the timed steps")
     p.add_argument("--no-block", action="store_true",
                    help="skip the layer-sequential decoder-block leg after the timed steps")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the per-layer runs of the 7B layer, 70B MLP and outlier workloads")
     p.add_argument("--cpu-tokens", type=int, default=16384)
     p.add_argument("--cpu-rows", type=int, default=128)
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -218,27 +220,31 @@ def awq_leg(G, torch, Wd, Xd, H, gptq_out, spec, n_grid=20):
                         "unit": "GB/s", "frac": am_gbs / PEAK["hbm"]}}
 
 
-def block_leg(G, torch, Xd, spec, seq_len=2048, d_ff=11008):
-    """Layer-sequential quantization of one LLaMA-7B-shaped decoder layer on the bench's tokens
+def block_leg(G, torch, dev, bits, seq_len=2048):
+    """Layer-sequential quantization of one LLaMA-7B-shaped decoder layer
     (block.quantize_decoder_block: q/k/v_proj on rmsnorm(x), o_proj on the attention output of
     the quantized q/k/v, gate/up_proj on rmsnorm of the residual, down_proj on the MLP product
-    of the quantized gate/up), with random fp16 weights ~ N(0, 0.02^2) and norm weights
-    exp(0.2 N(0, 1)).  Wall time from events on the launch stream, the time of each kernel
-    family, and the attention kernel against the fp32 MFMA peak (2 * 128 * l (l + 1) flops
-    per head and sequence of l tokens: q.k and p.v over the causal pairs) and the forward
-    products (fp16 activations times the codes as fp16 integers, 2 n_tok d (4 d + 2 d_ff)
-    flops) against the fp16 MFMA peak."""
+    of the quantized gate/up) on the 7B-layer workload's seeded inputs: its sub-layer weights,
+    its 131072 calibration tokens (64 sequences of 2048) as the layer input, norm weights
+    exp(0.2 N(0, 1)); asymmetric g128, B = 128.  Wall time from events on the launch stream,
+    the time of each kernel family, and the attention kernel against the fp32 MFMA peak
+    (2 * 128 * l (l + 1) flops per head and sequence of l tokens: q.k and p.v over the causal
+    pairs) and the forward products (fp16 activations times the codes as fp16 integers,
+    2 n_tok d (4 d + 2 d_ff) flops) against the fp16 MFMA peak."""
     from post_weight_quantization_24_amd import block as BLK
-    n_tok, d = Xd.shape
-    dev = Xd.device
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(7)
-    shapes = {"q_proj": (d, d), "k_proj": (d, d), "v_proj": (d, d), "o_proj": (d, d),
-              "gate_proj": (d_ff, d), "up_proj": (d_ff, d), "down_proj": (d, d_ff)}
-    W = {k: (torch.randn(s, generator=gen, device=dev) * 0.02).to(torch.float16)
-         for k, s in shapes.items()}
-    g1, g2 = (torch.exp(0.2 * torch.randn(d, generator=gen, device=dev)).to(torch.float16)
-              for _ in range(2))
+    from post_weight_quantization_24_amd import synth
+    wl = synth.WORKLOADS["llama7b_layer"]
+    d, d_ff = wl.layer("q_proj").d_col, wl.layer("gate_proj").d_row
+    n_tok = wl.n_tok
+    Xd = torch.empty((n_tok, d), dtype=torch.float16, device=dev)
+    for t in range(0, n_tok, 32768):
+        part = synth.layer_acts(wl, "attn_in", n_tok=min(32768, n_tok - t), tok_start=t)
+        Xd[t:t + part.shape[0]].copy_(torch.from_numpy(part))
+    shapes = {l.name: (l.d_row, l.d_col) for l in wl.layers}
+    W = {k: torch.from_numpy(synth.layer_weight(wl, k)).to(dev) for k in shapes}
+    g1, g2 = (torch.from_numpy(synth.gen_norm_weight(wl.wid, nm, d)).to(dev)
+              for nm in ("input_layernorm", "post_attention_layernorm"))
+    spec = G.Spec.make(bits, wl.group, wl.sym, 128, wl.damp)
     BLK.quantize_decoder_block(W, Xd, g1, g2, spec, seq_len)          # warm-up
     torch.cuda.synchronize()
     G.profile_reset()
@@ -267,9 +273,9 @@ def block_leg(G, torch, Xd, spec, seq_len=2048, d_ff=11008):
     ms_f = sum(G.profile_read(f)[1] for f in ("block_gemm", "mlp_gemm"))
     fwd_tf = fwd_flops / (ms_f / 1e3) / 1e12
     weights = sum(a * b for a, b in shapes.values())
-    out = {"config": {"d": d, "d_ff": d_ff, "heads": d // 128, "seq_len": seq_len, "n_tok": n_tok,
-                      "bits": spec.bits, "group": spec.group, "sym": bool(spec.sym),
-                      "block": spec.block},
+    out = {"config": {"workload": wl.name, "d": d, "d_ff": d_ff, "heads": d // 128,
+                      "seq_len": seq_len, "n_tok": n_tok, "bits": spec.bits, "group": spec.group,
+                      "sym": bool(spec.sym), "block": spec.block},
            "ms": ms, "weights": weights, "weights_per_s": weights / (ms / 1e3),
            "families_ms": fams,
            "attention": {"launches": n_a, "ms": ms_a, "achieved": attn_tf, "peak": PEAK["mfma_f32"],
@@ -277,20 +283,165 @@ def block_leg(G, torch, Xd, spec, seq_len=2048, d_ff=11008):
            "forward_gemm": {"ms": ms_f, "achieved": fwd_tf, "peak": PEAK["mfma_f16"],
                             "unit": "TFLOP/s", "frac": fwd_tf / PEAK["mfma_f16"]},
            "losses": {k: r["loss_" + k] for k in shapes}}
-    del r, W
+    del r, W, Xd
     return out
+
+
+# Per-layer runs of the larger workloads: (workload, input, [(layer, k)], bit widths, blocks).
+# k = the number of sub-layers of a real model that share the layer's Hessian and G (q/k/v:
+# 3, gate/up: 2, every other layer 1); t_layer = t_hessian / k + t_prepare / k + t_quantize.
+CONFIG_RUNS = [
+    ("llama7b_layer", "attn_in", [("q_proj", 3), ("k_proj", 3), ("v_proj", 3), ("gate_proj", 2),
+                                  ("up_proj", 2)], (4, 3), (128,)),
+    ("llama7b_layer", "o_in", [("o_proj", 1)], (4, 3), (128,)),
+    ("llama7b_layer", "down_in", [("down_proj", 1)], (4, 3), (128,)),
+    ("llama70b_mlp", "mlp_in", [("gate_proj", 2), ("up_proj", 2)], (4,), (128,)),
+    ("llama70b_mlp", "down_in", [("down_proj", 1)], (4,), (128,)),
+    ("outlier_8192", "x", [("w", 1)], (2, 3), (32, 64, 128, 256)),
+]
+
+
+def progress(msg):
+    print("bench: " + msg, file=sys.stderr, flush=True)
+
+
+def configs_leg(G, torch, dev, reps=3):
+    """Every layer, bit width and block size of the four larger workloads at full size, on
+    their seeded inputs: the Hessian and the inverse factor once per calibration input, the
+    column solve once per layer, bit width and block size.  Wall times are medians of `reps`
+    runs between HIP events on the launch stream (after one warm-up); one more run with
+    every kernel family timed gives each phase's fraction of its roofline."""
+    import ctypes
+    from post_weight_quantization_24_amd import synth
+    out = []
+
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    def families(fn, fams):
+        G.profile_reset()
+        G.profile_only(None)
+        G.profile_enable(True)
+        fn()
+        torch.cuda.synchronize()
+        G.profile_enable(False)
+        return {f: G.profile_read(f) for f in fams}
+
+    for wl_name, xname, layers, bit_list, blocks in CONFIG_RUNS:
+        wl = synth.WORKLOADS[wl_name]
+        d, n_tok = wl.x_dim(xname), wl.n_tok
+        Xd = torch.empty((n_tok, d), dtype=torch.float16, device=dev)
+        for t in range(0, n_tok, 32768):
+            part = synth.layer_acts(wl, xname, n_tok=min(32768, n_tok - t), tok_start=t)
+            Xd[t:t + part.shape[0]].copy_(torch.from_numpy(part))
+        H = torch.empty((d, d), dtype=torch.float32, device=dev)
+        Gm = torch.empty_like(H)
+        L = G.lib()
+        ws_h = torch.empty(max(L.gptq_hessian_workspace_size(d, n_tok, d, 0), 256),
+                           dtype=torch.uint8, device=dev)
+        ws_p = torch.empty(L.gptq_prepare_workspace_size(d), dtype=torch.uint8, device=dev)
+
+        def run_h():
+            H.zero_()
+            G.hessian_accumulate(H, Xd, ws=ws_h)
+
+        def run_p():
+            G.prepare_hinv(H, G=Gm, damp_frac=wl.damp, ws=ws_p, check=False)
+
+        t_h = timed(run_h)
+        f_h = families(run_h, ("hessian_mfma", "hessian_reduce"))
+        t_p = timed(run_p)
+        G.prepare_hinv(H, G=Gm, damp_frac=wl.damp, ws=ws_p, check=True)   # pivots checked once
+        f_p = families(run_p, ("prep_damp", "prep_leaf", "prep_gemm"))
+        del Xd, ws_h
+        for layer_name, k in layers:
+            layer = wl.layer(layer_name)
+            d_row = layer.d_row
+            Wd = torch.from_numpy(synth.layer_weight(wl, layer_name)).to(dev)
+            for bits in bit_list:
+                for block in blocks:
+                    spec = G.Spec.make(bits, wl.group, wl.sym, block, wl.damp)
+                    g = d if wl.group == 0 else wl.group
+                    qw = torch.empty((d_row, d * bits // 32), dtype=torch.int32, device=dev)
+                    sc = torch.empty((d_row, d // g), dtype=torch.float32, device=dev)
+                    ze = torch.empty((d_row, d // g), dtype=torch.uint8, device=dev)
+                    esq = torch.empty(d_row, dtype=torch.float64, device=dev)
+                    ws_q = torch.empty(L.gptq_quantize_workspace_size(d_row, d, ctypes.byref(spec)),
+                                       dtype=torch.uint8, device=dev)
+
+                    def run_q():
+                        G.quantize_layer(Wd, Gm, spec, qweight=qw, scales=sc, zeros=ze,
+                                         err_sq=esq, ws=ws_q)
+
+                    t_q = timed(run_q)
+                    f_q = families(run_q, ("quant_convert", "quant_group_params", "quant_block",
+                                           "lazy_gemm"))
+                    phases = {}
+                    for fam, (n, ms) in list(f_h.items()) + list(f_p.items()) + list(f_q.items()):
+                        if not n:
+                            continue
+                        work, unit, peak, bound = family_work(fam, d_row, d, n_tok, bits, block,
+                                                              "f16")
+                        ach = work / (ms / 1e3) / (1e12 if unit == "TFLOP/s" else 1e9)
+                        phases[fam] = {"ms": ms, "launches": n, "bound": bound, "achieved": ach,
+                                       "unit": unit, "frac": ach / peak}
+                    t_layer = t_h / k + t_p / k + t_q
+                    out.append({
+                        "workload": wl_name, "layer": layer_name, "d_row": d_row, "d_col": d,
+                        "n_tok": n_tok, "bits": bits, "group": wl.group, "sym": bool(wl.sym),
+                        "block": block, "k_shared": k, "hessian_ms": t_h, "prepare_ms": t_p,
+                        "quantize_ms": t_q, "t_layer_ms": t_layer,
+                        "weights_per_s": d_row * d / (t_layer / 1e3),
+                        "quantize_only_weights_per_s": d_row * d / (t_q / 1e3),
+                        "phases": phases})
+                    del qw, sc, ze, esq, ws_q
+                    progress("%s %s INT%d B=%d: %.2f ms per layer" % (wl_name, layer_name, bits,
+                                                                      block, t_layer))
+            del Wd
+        del H, Gm, ws_p
+        torch.cuda.empty_cache()
+    return out
+
+
+def host_description():
+    """os.cpu_count(), the CPU model from /proc/cpuinfo and the threads of the host BLAS
+    libraries the oracle uses (numpy's and torch's)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = {}
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            blas["%s:%s" % (i.get("user_api"), i.get("internal_api"))] = i.get("num_threads")
+    except Exception:  # pragma: no cover
+        pass
+    import torch
+    blas["torch"] = torch.get_num_threads()
+    return {"cpu_count": os.cpu_count(), "cpu_model": model, "blas_threads": blas}
 
 
 def cpu_baseline(W, X_sample, n_tok_full, spec, rows):
     """The oracle as it stands on a bounded sample: Hessian on X_sample (scaled to all tokens),
-    the inverse factor at full size, the column loop on `rows` rows (scaled to all rows)."""
-    import numpy as np
+    the inverse factor at full size, the column loop on `rows` rows (scaled to all rows).
+    `value` is the rate projected to the whole layer from the measured sample times."""
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    host = host_description()
     d_row, d_col = W.shape
     t0 = time.perf_counter()
     H = O.hessian(X_sample)
@@ -303,15 +454,19 @@ def cpu_baseline(W, X_sample, n_tok_full, spec, rows):
     O.gptq_quantize(W[:rows], Gm, spec["bits"], spec["group"], spec["sym"], block=spec["block"])
     t_q = time.perf_counter() - t0
     t_layer = t_h * (n_tok_full / X_sample.shape[0]) + t_p + t_q * (d_row / rows)
+    threads = max([v for v in host["blas_threads"].values() if v] + [1])
     return {
         "value": d_row * d_col / t_layer,
         "unit": "weights/s",
         "cores": threads,
         "kind": "oracle",
+        "projected": True,
         "sample": "Hessian on %d of %d tokens (x%.0f), inverse factor at full size, column loop "
                   "on %d of %d rows (x%.0f); measured %.1f s, projected %.1f s per layer"
                   % (X_sample.shape[0], n_tok_full, n_tok_full / X_sample.shape[0], rows, d_row,
                      d_row / rows, t_h + t_p + t_q, t_layer),
+        "measured_s": {"hessian": t_h, "prepare": t_p, "column_loop": t_q},
+        "host": host,
     }
 
 
@@ -400,6 +555,7 @@ def main():
                           "avg_launch_ms": ms / n}
         return out
 
+    progress("inputs resident, warm-up done")
     # ---- one untimed step with every kernel family timed: the phase table
     G.profile_reset()
     G.profile_only(None)
@@ -431,6 +587,7 @@ def main():
     G.profile_enable(False)
     G.profile_only(None)
     ms_per_step = elapsed * 1e3 / a.steps
+    progress("timed steps: %.3f ms per step" % ms_per_step)
     timed = read_phases(a.steps)[dom]
     avg_s = timed["avg_launch_ms"] / 1e3
     launches_per_step = timed["launches_per_step"]
@@ -476,8 +633,8 @@ def main():
         nb = 2048
         xm = torch.randn((nb, big_cols), device=dev).to(torch.float16)
         ym = torch.empty((nb, big_rows), dtype=torch.float32, device=dev)
-        wsm = torch.empty(G.lib().gptq_dequant_matmul_workspace_size(big_rows, big_cols),
-                          dtype=torch.uint8, device=dev)
+        wsm = torch.empty(max(G.lib().gptq_dequant_matmul_workspace_size(big_rows, big_cols, 4, 128),
+                              256), dtype=torch.uint8, device=dev)
         for _ in range(2):
             G.dequant_matmul(bq, bs, bz, xm, 4, 128, big_cols, y=ym, ws=wsm)
         torch.cuda.synchronize()
@@ -499,7 +656,10 @@ def main():
         torch.cuda.synchronize()
         lib_ms = e0.elapsed_time(e1) / 10
         tf = flops / (ms_m / n_m / 1e3) / 1e12
-        w4[-1]["batched"] = {"n": nb, "product_ms": ms_m / n_m, "expand_ms": ms_e / n_e,
+        w4[-1]["batched"] = {"n": nb, "product_ms": ms_m / n_m,
+                             "expand_ms": ms_e / n_e if n_e else 0.0,
+                             "workspace_bytes": G.lib().gptq_dequant_matmul_workspace_size(
+                                 big_rows, big_cols, 4, 128),
                              "achieved": tf, "peak": PEAK["mfma_f16"], "unit": "TFLOP/s",
                              "frac": tf / PEAK["mfma_f16"], "fp16_library_ms": lib_ms}
         del w16, xb, xm, ym, wsm, bq, bs, bz
@@ -508,15 +668,27 @@ def main():
     awq = None
     if not a.no_awq:
         awq = awq_leg(G, torch, Wd, Xd, H, (qweight, scales, zeros), spec)
+        progress("awq leg done")
 
     # ---- one decoder layer quantized layer by layer on the same tokens (7B shapes)
     blk = None
-    if not a.no_block and d_col == 4096 and Xd.dtype == torch.float16:
-        blk = block_leg(G, torch, Xd, G.Spec.make(4, 128, False, 128, wl.damp))
+    if not a.no_block:
+        blk = []
+        for b in (4, 3):
+            blk.append(block_leg(G, torch, dev, b))
+            progress("decoder block INT%d: %.1f ms" % (b, blk[-1]["ms"]))
+
+    # ---- every layer, bit width and block size of the larger workloads
+    cfgs = None
+    if not a.no_configs:
+        del Xd
+        torch.cuda.empty_cache()
+        cfgs = configs_leg(G, torch, dev)
 
     cpu = None
     if not a.no_cpu:
         cpu = cpu_baseline(W, X_sample, n_tok, spec_d, min(a.cpu_rows, d_row))
+        progress("cpu baseline done")
 
     out = {
         "metric": METRIC,
@@ -543,6 +715,10 @@ def main():
         "w4a16": w4,
         "awq": awq,
         "decoder_block": blk,
+        "configs": cfgs,
+        "step": "H = 0; H += 2 X^T X over all tokens; G = Cholesky((H + lambda I)^-1)^T; "
+                "column solve with packing.  The positive-pivot check of G (one wait of the host "
+                "on the stream) runs in the warm-up steps, not in the timed ones.",
         "input_gen_s": gen_s,
     }
     print(json.dumps(out))

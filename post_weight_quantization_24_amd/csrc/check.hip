@@ -1,7 +1,9 @@
 // Dequantization and the layer objective of page "量化", section GPTQ:
 // ||W X - W^ X||_F^2 = 1/2 * sum_r D_r H D_r^T with D = W - W^ and the undamped H = 2 X X^T.
-// W^ = s * (code - z) per row and group.  T = D H runs on the fp32 MFMA GEMM; the row
-// sums of T .* D and the total are accumulated in double in a fixed order.
+// W^ = s * (code - z) per row and group.  H is symmetric, so the loss comes from half the
+// product: 1/2 D H D^T = sum T .* D - 1/2 sum D^2 diag(H) per row, with T = D U and U the
+// upper triangle of H (the fp32 MFMA GEMM with a triangular operand mask); the row sums and
+// the total are accumulated in double in a fixed order.
 
 #include "gptq_internal.h"
 

@@ -82,3 +82,16 @@ def test_salient_channels_protected():
     r = O.awq_search(W, H, O.act_absmean(X), 4, 128, False)
     assert r["alpha"] > 0
     assert r["losses"][r["best"]] < 0.5 * r["losses"][0]
+
+
+def test_scales_hand_values():
+    """s = s_X^alpha at an interior exponent, by hand: s_X = [4, 1, 9, 0.25, 0] at alpha = 1/2
+    gives [2, 1, 3, 0.5, 1] (the all-zero channel keeps 1); at alpha = 1/4, 16 -> 2 and
+    81 -> 3; at alpha = 1 s_X itself (rounded to float32)."""
+    s = O.awq_scales(np.array([4.0, 1.0, 9.0, 0.25, 0.0]), 0.5)
+    assert s.dtype == np.float32
+    np.testing.assert_array_equal(s, np.array([2.0, 1.0, 3.0, 0.5, 1.0], np.float32))
+    np.testing.assert_array_equal(O.awq_scales(np.array([16.0, 81.0]), 0.25),
+                                  np.array([2.0, 3.0], np.float32))
+    np.testing.assert_array_equal(O.awq_scales(np.array([0.1, 7.0]), 1.0),
+                                  np.array([0.1, 7.0], np.float32))
