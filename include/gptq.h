@@ -239,6 +239,21 @@ int gptq_dequant_matmul(const uint32_t* qweight, const float* scales, const uint
 size_t gptq_act_absmean_workspace_size(int64_t d, int64_t n_tok);
 int gptq_act_absmean(double* sx_sum, int64_t d, const void* X, int x_dtype, int64_t n_tok,
                      int64_t ldx, void* ws, size_t ws_bytes, void* stream);
+/* gptq_act_absmean_noalloc: gptq_act_absmean without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight calibration loops,
+ * harnesses that forbid hipMalloc).  The same kernels and the same result bit for bit.
+ *   Arguments as for gptq_act_absmean; the call runs on `stream`, which must belong to the
+ *   current device (NULL: the current device's null stream).
+ *   Scratch: the per-split partial sums live in a 16 MiB array the library holds on each GPU
+ *   it runs on until the process ends (its address is looked up on the first call on a
+ *   device).  Every shape the call accepts fits; a plan that would need more is rejected with
+ *   GPTQ_EINVAL.  The call allocates nothing (no hipMalloc, no hipFree).
+ *   Calls that overlap on one GPU (on different streams, or from several threads) share that
+ *   array and race; serialize them.  Each call writes every partial sum it reads, so nothing
+ *   needs clearing between calls.
+ * Errors: GPTQ_EINVAL (as gptq_act_absmean; a stream of another device), GPTQ_EHIP. */
+int gptq_act_absmean_noalloc(double* sx_sum, int64_t d, const void* X, int x_dtype,
+                             int64_t n_tok, int64_t ldx, void* stream);
 size_t gptq_awq_workspace_size(int64_t d_row, int64_t d_col);
 int gptq_awq_search(const void* W, int w_dtype, int64_t d_row, int64_t d_col, const float* H,
                     const double* sx_sum, int64_t n_tok, const gptq_spec* spec, int n_grid,

@@ -381,6 +381,43 @@ int gptq_act_absmean(double* sx_sum, int64_t d, const void* X, int x_dtype, int6
   return GPTQ_OK;
 }
 
+int gptq_act_absmean_noalloc(double* sx_sum, int64_t d, const void* X, int x_dtype,
+                             int64_t n_tok, int64_t ldx, void* stream) {
+  g_last_error.clear();
+  if (d < 1 || d > (int64_t)1 << 20) return fail(GPTQ_EINVAL, "d out of range (%lld)", (long long)d);
+  if (n_tok < 0) return fail(GPTQ_EINVAL, "n_tok < 0");
+  if (x_dtype != GPTQ_F16 && x_dtype != GPTQ_F32) return fail(GPTQ_EINVAL, "x_dtype must be F16 or F32");
+  if (!sx_sum) return fail(GPTQ_EINVAL, "sx_sum is NULL");
+  if (n_tok == 0) return GPTQ_OK;
+  if (!X) return fail(GPTQ_EINVAL, "X is NULL");
+  if (ldx < d) return fail(GPTQ_EINVAL, "ldx (%lld) < d (%lld)", (long long)ldx, (long long)d);
+  const size_t elt = x_dtype == GPTQ_F16 ? 2 : 4;
+  if (!aligned(X, 16) || (ldx * (int64_t)elt) % 16 != 0)
+    return fail(GPTQ_EINVAL, "X and its rows must be 16-byte aligned");
+  const size_t need = gptq::absmean_ws_bytes(d, n_tok);
+  if (need > gptq::absmean_scratch_bytes())
+    return fail(GPTQ_EINVAL, "needs %zu bytes of scratch, more than the %zu the library holds",
+                need, gptq::absmean_scratch_bytes());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "gptq_act_absmean_noalloc: hipGetDevice");
+  if (st) {
+    hipDevice_t sdev = -1;
+    if ((e = hipStreamGetDevice(st, &sdev)) != hipSuccess)
+      return hip_fail(e, "gptq_act_absmean_noalloc: hipStreamGetDevice");
+    if (sdev != dev)
+      return fail(GPTQ_EINVAL, "the stream belongs to device %d, the current device is %d",
+                  (int)sdev, dev);
+  }
+  void* ws = nullptr;
+  if ((e = gptq::absmean_scratch_ptr(dev, &ws)) != hipSuccess)
+    return hip_fail(e, "gptq_act_absmean_noalloc: scratch address");
+  e = gptq::absmean_launch(sx_sum, d, X, x_dtype, n_tok, ldx, ws, st);
+  if (e != hipSuccess) return hip_fail(e, "gptq_act_absmean_noalloc");
+  return GPTQ_OK;
+}
+
 size_t gptq_awq_workspace_size(int64_t d_row, int64_t d_col) {
   if (check_layer(GPTQ_F32, d_row, d_col) != GPTQ_OK) {
     g_last_error.clear();

@@ -18,8 +18,18 @@
 // division, the scales s in double and rounded to float32.
 
 #include <cmath>
+#include <mutex>
 
 #include "gptq_internal.h"
+
+// Scratch of the allocation-free magnitude sums (gptq_act_absmean_noalloc): the per-split
+// partial sums, in an array the library owns for the life of the process, one copy per GPU.
+// Its size covers every shape the call accepts (the planner keeps splits x d below
+// 2^20 + d doubles for d <= 2^20), so no caller ever hits the limit in practice; the call
+// still checks it.  Host code never passes the array's name to a kernel: it is a host-side
+// stand-in, not a device address.  The device address comes from hipGetSymbolAddress, once
+// per device.
+static __device__ __align__(256) double scratch[(size_t)1 << 21];
 
 namespace gptq {
 
@@ -300,6 +310,30 @@ hipError_t absmean_launch(double* sx_sum, int64_t d, const void* X, int x_dtype,
   hipLaunchKernelGGL(absmean_reduce, dim3((unsigned)ceil_div(d, 64)), dim3(AM_THREADS), 0,
                      stream, part, p.splits, d, sx_sum);
   return hipGetLastError();
+}
+
+size_t absmean_scratch_bytes() { return sizeof(scratch); }
+
+namespace {
+std::mutex g_scratch_mu;
+constexpr int MAX_DEVICES = 64;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+}  // namespace
+
+// The device address of this device's copy of `scratch`, looked up on the first call on each
+// device (with that device current) and kept.
+hipError_t absmean_scratch_ptr(int device, void** out) {
+  if (device < 0 || device >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = p;
+  }
+  *out = g_scratch_ptr[device];
+  return hipSuccess;
 }
 
 size_t awq_ws_bytes(int64_t d_row, int64_t d_col) {

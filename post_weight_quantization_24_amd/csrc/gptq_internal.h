@@ -86,6 +86,9 @@ hipError_t loss_of_diff_upper(const float* D, const float* H, int64_t d_row, int
 
 // ---------------------------------------------------------------- AWQ scale search (awq.hip)
 size_t absmean_ws_bytes(int64_t d, int64_t n_tok);
+// The allocation-free variant's scratch: its size in bytes, and this device's address of it.
+size_t absmean_scratch_bytes();
+hipError_t absmean_scratch_ptr(int device, void** out);
 hipError_t absmean_launch(double* sx_sum, int64_t d, const void* X, int x_dtype, int64_t n_tok,
                           int64_t ldx, void* ws, hipStream_t stream);
 size_t awq_ws_bytes(int64_t d_row, int64_t d_col);

@@ -60,6 +60,7 @@ _SIGS = {
                              _vp, _sz, _vp], _int),
     "gptq_act_absmean_workspace_size": ([_i64, _i64], _sz),
     "gptq_act_absmean": ([_vp, _i64, _vp, _int, _i64, _i64, _vp, _sz, _vp], _int),
+    "gptq_act_absmean_noalloc": ([_vp, _i64, _vp, _int, _i64, _i64, _vp], _int),
     "gptq_awq_workspace_size": ([_i64, _i64], _sz),
     "gptq_awq_search": ([_vp, _int, _i64, _i64, _vp, _vp, _i64, ctypes.POINTER(Spec), _int, _vp,
                          _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
@@ -290,6 +291,17 @@ def act_absmean(sx_sum, X, ws=None, stream=None):
     _check(lib().gptq_act_absmean(sx_sum.data_ptr(), d, X.data_ptr(), _dtype_code(X), n_tok,
                                   X.stride(0), ws.data_ptr(), ws.numel() * ws.element_size(),
                                   _stream_handle(stream)))
+    return sx_sum
+
+
+@_streamed
+def act_absmean_noalloc(sx_sum, X, stream=None):
+    """sx_sum [d] float64 += sum over the rows of X of |x|, with the library's own scratch
+    (gptq_act_absmean_noalloc: no workspace, nothing allocated)."""
+    d = sx_sum.shape[0]
+    assert X.dim() == 2 and X.shape[1] == d and X.stride(1) == 1 and sx_sum.is_contiguous()
+    _check(lib().gptq_act_absmean_noalloc(sx_sum.data_ptr(), d, X.data_ptr(), _dtype_code(X),
+                                          X.shape[0], X.stride(0), _stream_handle(stream)))
     return sx_sum
 
 

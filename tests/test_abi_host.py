@@ -293,3 +293,20 @@ def test_dequant_matmul_validation(lib):
     assert call(ldx=(1 << 22) + 8) == G.EINVAL
     assert call(n=0) == G.OK
 
+
+def test_absmean_noalloc_validation(lib):
+    f = lib.gptq_act_absmean_noalloc
+    assert f(FAKE, 0, FAKE, 0, 10, 8, None) == G.EINVAL
+    assert b"d out of range" in lib.gptq_last_error()
+    assert f(None, 16, FAKE, 0, 10, 16, None) == G.EINVAL
+    assert f(FAKE, 16, FAKE, 2, 10, 16, None) == G.EINVAL
+    assert f(FAKE, 16, None, 0, 10, 16, None) == G.EINVAL
+    assert f(FAKE, 16, FAKE, 0, -1, 16, None) == G.EINVAL
+    assert f(FAKE, 16, FAKE, 0, 10, 8, None) == G.EINVAL           # ldx < d
+    assert f(FAKE, 12, FAKE, 0, 10, 12, None) == G.EINVAL          # rows not 16-byte aligned
+    assert f(FAKE, 16, FAKE, 0, 0, 16, None) == G.OK               # empty chunk: no HIP call
+    # the scratch the library holds covers the largest plan of every accepted shape
+    need = max(lib.gptq_act_absmean_workspace_size(d, n)
+               for d in (1, 7, 100, 511, 512, 4096, 11008, 28672, 1 << 20)
+               for n in (1, 300, 65536, 1 << 20, 1 << 26))
+    assert need <= 16 << 20
