@@ -19,6 +19,7 @@
 // the same addresses).  Column q is quantized by its owner lane; its e reaches the
 // other 15 lanes with one DPP row broadcast.
 
+#include <mutex>
 #include <utility>
 
 #include "gptq_internal.h"
@@ -352,13 +353,22 @@ size_t quant_block_lds() {
 template <int B>
 hipError_t launch_block(const QuantArgs& a, const float* Wc, float* E, int64_t j0, int width,
                         hipStream_t s) {
-  static bool attr = false;
+  // the dynamic LDS limit is raised once per device (callers on several threads share it)
+  static std::mutex mu;
+  static bool attr[64] = {};
   const size_t lds = quant_block_lds<B>();
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(quant_block<B>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr = true;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    if (!attr[dev]) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(quant_block<B>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      attr[dev] = true;
+    }
   }
   const int64_t g = a.group == 0 ? a.d_col : a.group;
   const int64_t n_groups = a.d_col / g;
