@@ -56,7 +56,12 @@ template <int BM, int BN, bool TA, bool TB>
 struct Cfg {
   // K per LDS stage: 128 x 128 tiles keep 16 so that staging fits two waves per SIMD.
   static constexpr int BK = BM >= 128 ? 16 : 32;
-  static constexpr int LDA_S = BM + 4, LDB_S = BN + 4;
+  // Row strides of the k-major stages.  An operand stored with 16-byte writes (op(A) with
+  // TA, op(B) without TB) needs a stride that keeps them aligned: +4.  An operand stored one
+  // dword at a time has half a wave writing BK/4 k-rows, 4 apart, of 128/BK consecutive
+  // columns each; +1 (BK = 32) or +2 (BK = 16) puts those rows on disjoint runs of banks.
+  static constexpr int SPAD = BK == 32 ? 1 : 2;
+  static constexpr int LDA_S = TA ? BM + 4 : BM + SPAD, LDB_S = TB ? BN + SPAD : BN + 4;
   static constexpr int A_V4 = BM * BK / 4 / 256;   // float4 per thread for the A stage
   static constexpr int B_V4 = BN * BK / 4 / 256;
   static constexpr int TM = BM / 64, TN = BN / 64;  // 32x32 MFMA tiles per wave
@@ -236,7 +241,10 @@ __device__ __forceinline__ void gemm_tile(const Dev& g, int64_t tile, Smem<BM, B
     const float* bs = Bs[buf];
 #pragma unroll
     for (int kk = 0; kk < BK / 2; ++kk) {
-      const int kr = 2 * kk + (lane >> 5);
+      // k of this step for lane half h: (kk % 8) + 8 h + 16 (kk / 8).  Any one-to-one choice
+      // sums the same products; this one lets consecutive steps' reads pair into one
+      // two-address LDS read.
+      const int kr = (kk & 7) + 8 * (lane >> 5) + 16 * (kk >> 3);
       float a[C::TM], b[C::TN];
 #pragma unroll
       for (int t = 0; t < C::TM; ++t) a[t] = as[kr * C::LDA_S + wm * (BM / 2) + t * 32 + (lane & 31)];
@@ -454,53 +462,66 @@ __device__ __forceinline__ void dma_tile(const Dev& g, int64_t tile, char* ring)
     const char* sb = sa + C::A_BYTES;
     const int64_t k0 = k_lo + (int64_t)s * DBK;
     const bool msk = masked(s);
+    // the stage's operands first (one LDS wait), then its 8 k-steps of MFMAs
+    floatx4 a[DBK / 8][C::TM], b[DBK / 8][C::TN];
 #pragma unroll
     for (int u = 0; u < DBK / 8; ++u) {
       const int c = 2 * u + h;                     // chunk: k = 4c .. 4c + 3
-      floatx4 a[C::TM];
 #pragma unroll
       for (int x = 0; x < C::TM; ++x) {
         const int row = wm * (BM / 2) + 32 * x + l32;
-        a[x] = *reinterpret_cast<const floatx4*>(sa + row * 64 + 16 * (c ^ ((row >> 2) & 3)));
-        if (msk) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int64_t mg = m0 + row, kg = k0 + 4 * c + e;
-            if (!a_ok(g, mg, kg) || kg < k_lo) a[x][e] = 0.0f;
-          }
-        }
-        a[x] = a[x] * g.alpha;
+        a[u][x] = *reinterpret_cast<const floatx4*>(sa + row * 64 + 16 * (c ^ ((row >> 2) & 3)));
       }
-      floatx4 b[C::TN];
 #pragma unroll
       for (int y = 0; y < C::TN; ++y) {
         const int col = wn * (BN / 2) + 32 * y + l32;
         if (TB) {
-          b[y] = *reinterpret_cast<const floatx4*>(sb + col * 64 + 16 * (c ^ ((col >> 2) & 3)));
+          b[u][y] = *reinterpret_cast<const floatx4*>(sb + col * 64 + 16 * (c ^ ((col >> 2) & 3)));
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int kr = 4 * c + e;
-            b[y][e] = *reinterpret_cast<const float*>(
+            b[u][y][e] = *reinterpret_cast<const float*>(
                 sb + (kr / nc_rows(BN)) * (1024 + nc_pad(BN)) + (kr % nc_rows(BN)) * BN * 4 + col * 4);
           }
         }
-        if (msk) {
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < DBK / 8; ++u) {
+      const int c = 2 * u + h;
+      if (msk) {
+#pragma unroll
+        for (int x = 0; x < C::TM; ++x) {
+          const int row = wm * (BM / 2) + 32 * x + l32;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t mg = m0 + row, kg = k0 + 4 * c + e;
+            if (!a_ok(g, mg, kg) || kg < k_lo) a[u][x][e] = 0.0f;
+          }
+        }
+#pragma unroll
+        for (int y = 0; y < C::TN; ++y) {
+          const int col = wn * (BN / 2) + 32 * y + l32;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int64_t kg = k0 + 4 * c + e, ng = n0 + col;
-            if (!b_ok(g, kg, ng) || kg < k_lo) b[y][e] = 0.0f;
+            if (!b_ok(g, kg, ng) || kg < k_lo) b[u][y][e] = 0.0f;
           }
         }
       }
+#pragma unroll
+      for (int x = 0; x < C::TM; ++x) a[u][x] = a[u][x] * g.alpha;
+    }
+#pragma unroll
+    for (int u = 0; u < DBK / 8; ++u)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
 #pragma unroll
         for (int x = 0; x < C::TM; ++x)
 #pragma unroll
           for (int y = 0; y < C::TN; ++y)
-            acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[x][e], b[y][e], acc[x][y], 0, 0, 0);
-    }
+            acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u][x][e], b[u][y][e], acc[x][y], 0, 0, 0);
   }
 
   // epilogue: C = alpha op(A) op(B) (+ C when beta = 1); alpha was applied to op(A)
