@@ -387,18 +387,23 @@ hess_reduce(const float* __restrict__ part, int splits, int tiles, int64_t d,
   const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
   const bool diag = (r0 == c0);
   const int64_t sstride = (int64_t)tiles * TILE * TILE;   // between the splits of one tile
-  const float* pt = part + (int64_t)tile * TILE * TILE + (int64_t)(sa * 64) * TILE + sbk * 64 + tx;
-  // four rows (ty + 16 q) and four splits per step: 16 loads in flight per lane; each row's
-  // sum keeps split order
-  for (int rb = ty; rb < 16; rb += 4) {
-    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  // four columns 4 tq .. 4 tq + 3 of rows ty4 + 16 q (q = 0..3) per thread, four splits per
+  // step: 16 loads of 16 bytes in flight per lane; each element's sum keeps split order
+  const int tq = threadIdx.x % 16, ty4 = threadIdx.x / 16;
+  const float* pq = part + (int64_t)tile * TILE * TILE + (int64_t)(sa * 64) * TILE + sbk * 64 + 4 * tq;
+  const bool h_vec = (d & 3) == 0 && ((reinterpret_cast<uintptr_t>(H) & 15) == 0);
+  {
+    floatx4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     int sp = 0;
     for (; sp + 4 <= splits; sp += 4) {
-      float a[4][4];
+      floatx4 a[4][4];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) a[q][k] = pt[(rb + 16 * q) * TILE + (sp + k) * sstride];
+        for (int k = 0; k < 4; ++k)
+          a[q][k] = *reinterpret_cast<const floatx4*>(pq + (ty4 + 16 * q) * TILE + (sp + k) * sstride);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -406,14 +411,25 @@ hess_reduce(const float* __restrict__ part, int splits, int tiles, int64_t d,
     }
     for (; sp < splits; ++sp)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] += pt[(rb + 16 * q) * TILE + sp * sstride];
+      for (int q = 0; q < 4; ++q)
+        v[q] += *reinterpret_cast<const floatx4*>(pq + (ty4 + 16 * q) * TILE + sp * sstride);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int rr = rb + 16 * q;
-      const float w = 2.0f * v[q];
-      s[rr][tx] = w;
-      const int64_t i = r0 + rr, j = c0 + tx;
-      if (i < d && j < d && (!diag || j <= i)) H[i * d + j] += w;
+      const int rr = ty4 + 16 * q;
+      const floatx4 w = 2.0f * v[q];
+      const int64_t i = r0 + rr, j0 = c0 + 4 * tq;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) s[rr][4 * tq + c] = w[c];
+      if (h_vec && i < d && j0 + 3 < d && (!diag || j0 + 3 <= i)) {
+        floatx4* hp = reinterpret_cast<floatx4*>(H + i * d + j0);
+        *hp = *hp + w;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int64_t j = j0 + c;
+          if (i < d && j < d && (!diag || j <= i)) H[i * d + j] += w[c];
+        }
+      }
     }
   }
   __syncthreads();

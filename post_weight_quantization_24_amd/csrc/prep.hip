@@ -76,6 +76,48 @@ __global__ void __launch_bounds__(256) zero_lower(float* __restrict__ G, int64_t
       G[i * d + j] = 0.0f;
 }
 
+// The same two passes with 16-byte accesses (d % 4 == 0, H and G 16-byte aligned): rows
+// stride over the workgroups, four columns per thread; the quad that holds the diagonal is
+// written element by element, so nothing left of the diagonal (copy) or right of it (zero)
+// is touched.
+__global__ void __launch_bounds__(256)
+copy_damp4(const float* H, float* G, int64_t d, const double* lambda) {
+  const float lam = (float)*lambda;
+  const int64_t nq = d / 4;
+  for (int64_t i = blockIdx.x; i < d; i += gridDim.x) {
+    const floatx4* hr = reinterpret_cast<const floatx4*>(H + i * d);
+    floatx4* gr = reinterpret_cast<floatx4*>(G + i * d);
+    const int64_t qd = i / 4;
+    for (int64_t q = qd + threadIdx.x; q < nq; q += 256) {
+      const floatx4 v = hr[q];
+      if (q == qd) {
+        const int k = (int)(i - 4 * qd);   // the diagonal's place in the quad
+        float* g = G + i * d + 4 * qd;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (c >= k) g[c] = c == k ? v[c] + lam : v[c];
+      } else {
+        gr[q] = v;
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) zero_lower4(float* __restrict__ G, int64_t d) {
+  const floatx4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int64_t i = blockIdx.x; i < d; i += gridDim.x) {
+    floatx4* gr = reinterpret_cast<floatx4*>(G + i * d);
+    const int64_t qd = i / 4;
+    for (int64_t q = threadIdx.x; q <= qd; q += 256) {
+      if (q < qd) {
+        gr[q] = z;
+      } else {
+        for (int64_t j = 4 * qd; j < i; ++j) G[i * d + j] = 0.0f;
+      }
+    }
+  }
+}
+
 dim3 rows_grid(int64_t rows, int64_t cols) {
   const int64_t gx = (cols + 255) / 256;
   return dim3((unsigned)(gx < 1 ? 1 : gx > 64 ? 64 : gx), (unsigned)(rows > 32768 ? 32768 : rows));
@@ -410,18 +452,27 @@ hipError_t prepare_launch(const float* H, float* G, int64_t d, float damp_frac, 
                           hipStream_t stream) {
   hipError_t e;
   PrepWs w = carve(ws, d);
+  const bool vec4 = d % 4 == 0 && ((reinterpret_cast<uintptr_t>(H) | reinterpret_cast<uintptr_t>(G)) & 15) == 0;
   {
     ProfScope ps("prep_damp", stream);
     hipLaunchKernelGGL(damp_lambda, dim3(1), dim3(256), 0, stream, H, d, damp_frac, w.lambda,
                        w.flag);
-    hipLaunchKernelGGL(copy_damp, rows_grid(d, d), dim3(256), 0, stream, H, G, d, w.lambda);
+    if (vec4)
+      hipLaunchKernelGGL(copy_damp4, dim3((unsigned)(d < 16384 ? d : 16384)), dim3(256), 0, stream, H,
+                         G, d, w.lambda);
+    else
+      hipLaunchKernelGGL(copy_damp, rows_grid(d, d), dim3(256), 0, stream, H, G, d, w.lambda);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t p = d > NB ? split_of(d) * (d - split_of(d)) : 0;
   if ((e = factor_rec(G, d, 0, d, w.tmp, w.tmp + align_up((size_t)p, 64), w.flag, stream)) !=
       hipSuccess)
     return e;
-  hipLaunchKernelGGL(zero_lower, rows_grid(d, d), dim3(256), 0, stream, G, d);
+  if (vec4)
+    hipLaunchKernelGGL(zero_lower4, dim3((unsigned)(d < 16384 ? d : 16384)), dim3(256), 0, stream, G,
+                       d);
+  else
+    hipLaunchKernelGGL(zero_lower, rows_grid(d, d), dim3(256), 0, stream, G, d);
   return hipGetLastError();
 }
 
