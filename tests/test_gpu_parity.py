@@ -47,9 +47,10 @@ def codes_of(qweight, bits, d_col):
 
 # ------------------------------------------------------------------ a1 Hessian
 
+# d = 130 (not a multiple of 4) takes the reduction's element-wise writes of H
 @pytest.mark.parametrize("d,n_tok,dtype,ldx", [(320, 5000, "f16", 320), (200, 3000, "f16", 208),
                                                 (256, 1024, "f32", 256), (4096, 8192, "f16", 4096),
-                                                (96, 70000, "f16", 96)])
+                                                (96, 70000, "f16", 96), (130, 3000, "f16", 136)])
 def test_hessian(d, n_tok, dtype, ldx):
     torch = _torch()
     say("hessian", d, n_tok, dtype, ldx)
@@ -107,7 +108,9 @@ def _workload_h(d, n_tok, wid=93, outlier_frac=0.0):
     return O.hessian(X)
 
 
-@pytest.mark.parametrize("d", [100, 128, 200, 320, 1024])
+# d = 99 and 130 (not multiples of 4) take the element-wise copy and clear; the others the
+# 16-byte ones
+@pytest.mark.parametrize("d", [99, 100, 128, 130, 200, 320, 1024])
 def test_prepare_against_oracle(d):
     torch = _torch()
     say("prepare", d)
