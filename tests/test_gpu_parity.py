@@ -166,7 +166,7 @@ QUANT_CASES = [
     (80, 512, 3, 0, 1, 32, "f16"),
     (80, 768, 4, 64, 0, 256, "f16"),
     (33, 256, 2, 16, 1, 64, "f32"),
-    # two row chains on streams of their own (d_row >= 4096), a ragged split of the rows
+    # 4100 rows (a last workgroup of 4 rows) and 4096 rows at B = 64, per channel
     (4100, 640, 4, 128, 0, 128, "f16"),
     (4096, 384, 3, 0, 0, 64, "f16"),
 ]
