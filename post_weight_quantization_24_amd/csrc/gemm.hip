@@ -294,13 +294,14 @@ __global__ void __launch_bounds__(256, 2) gemm_f32_pair(Dev g1, int64_t tiles1, 
 
 // ---------------------------------------------------------------------------------
 // Direct-to-LDS variant (op(A) = A row-major M x K; B row-major K x N, or N x K with TB).
-// Operand tiles of 16 k per stage are copied from global memory straight into LDS by
-// buffer loads (`buffer_load_dwordx4 ... lds`, 1 KB per wave instruction), four stages in
-// the ring and three in flight, one barrier per stage.  A k-contiguous tile (A, or B with
-// TB) keeps 64-byte rows of 4 16-byte chunks whose slot is XOR-swizzled by (row / 4) % 4,
-// so a ds_read_b128 of one chunk per lane is conflict-free; an n-contiguous tile (B) keeps
-// its k rows with 64 or 128 bytes of padding per 1 KB copy, so that the two lane halves
-// (k and k + 4) read disjoint banks.  MFMA k index: lane half h, step 4u + e of a stage
+// Operand tiles of 32 k per stage are copied from global memory straight into LDS by
+// buffer loads (`buffer_load_dwordx4 ... lds`, 1 KB per wave instruction), two stages in
+// the ring and one in flight, one barrier per stage (a ring of four 16-k stages, three in
+// flight, took 3-4 % longer with twice the barriers per k; three 32-k stages, 6-24 %
+// longer).  A k-contiguous tile (A, or B with TB) keeps 128-byte rows of 8 16-byte chunks
+// whose slot is XOR-swizzled by (row / 2) % 8, so a ds_read_b128 of one chunk per lane is
+// conflict-free; an n-contiguous tile (B) keeps its k rows with 64 or 128 bytes of padding
+// per 1 KB copy, so that the two lane halves (k and k + 4) read disjoint banks.  MFMA k index: lane half h, step 4u + e of a stage
 // uses k = 4 (2u + h) + e, which lets the k-contiguous operand deliver four steps per
 // 16-byte read.  Global addresses are clamped into the operands and the stages that touch
 // an edge or a triangular mask zero the affected values after the LDS read.
@@ -334,20 +335,33 @@ __device__ __forceinline__ void stage_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-constexpr int DBK = 16;   // k per stage
-constexpr int DNS = 4;    // stages in the ring
+constexpr int DBK = 32;   // k per stage
+constexpr int DNS = 2;    // stages in the ring
 
 // n-contiguous tile of width W floats: rows per 1 KB copy, padding per copy, bytes
 __host__ __device__ constexpr int nc_rows(int W) { return 256 / W; }
 __host__ __device__ constexpr int nc_pad(int W) { return W == 128 ? 64 : 128; }
 __host__ __device__ constexpr int nc_bytes(int W) { return (DBK / nc_rows(W)) * (1024 + nc_pad(W)); }
 
+// k-contiguous rows: DBK floats, rows per 1 KB copy, 16-byte chunks per row, and the chunk
+// swizzle that keeps a ds_read_b128 of one chunk per lane conflict-free
+constexpr int KC_ROW = DBK * 4;
+constexpr int KC_RPC = 1024 / KC_ROW;
+constexpr int KC_CH = DBK / 4;
+static_assert(DBK == 16 || DBK == 32, "chunk swizzle defined for 16- and 32-deep stages");
+__device__ __forceinline__ int kc_swz(int row) {
+  // 16 consecutive rows (one 16-lane read group) land on 16 distinct 16-byte bank positions
+  // of the 256-byte bank row: the row's place in the bank row, and the swizzled chunk
+  return DBK == 16 ? (row >> 2) & 3 : (row >> 1) & (KC_CH - 1);
+}
+
 template <int BM, int BN, bool TB>
 struct DCfg {
-  static constexpr int A_BYTES = BM * 64;                        // k-contiguous
-  static constexpr int B_BYTES = TB ? BN * 64 : nc_bytes(BN);
+  static constexpr int A_BYTES = BM * KC_ROW;                    // k-contiguous
+  static constexpr int B_BYTES = TB ? BN * KC_ROW : nc_bytes(BN);
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int A_COPIES = BM / 16, B_COPIES = BN / 16;   // 1 KB copies per stage
+  static constexpr int A_COPIES = BM / KC_RPC;                   // 1 KB copies per stage
+  static constexpr int B_COPIES = TB ? BN / KC_RPC : DBK / nc_rows(BN);
   static constexpr int CPW = (A_COPIES + B_COPIES) / 4;          // per wave
   static constexpr int TM = BM / 64, TN = BN / 64;
   static_assert((A_COPIES + B_COPIES) % 4 == 0, "copies must split over 4 waves");
@@ -357,8 +371,8 @@ struct DCfg {
 // Rows >= row_lim and k >= k_lim are clamped (their values are masked later).
 __device__ __forceinline__ void copy_kc(rsrc_t rsrc, uint32_t lds, int q, int lane, int ld,
                                         int row_lim, int k_lim) {
-  const int row = 16 * q + (lane >> 2);
-  const int c = (lane & 3) ^ ((row >> 2) & 3);
+  const int row = KC_RPC * q + lane / KC_CH;
+  const int c = (lane % KC_CH) ^ kc_swz(row);
   const int r = row < row_lim ? row : row_lim - 1;
   const int k = 4 * c < k_lim ? 4 * c : k_lim - 4;
   dma16(rsrc, lds + q * 1024, (r * ld + k) * 4);
@@ -462,7 +476,7 @@ __device__ __forceinline__ void dma_tile(const Dev& g, int64_t tile, char* ring)
     const char* sb = sa + C::A_BYTES;
     const int64_t k0 = k_lo + (int64_t)s * DBK;
     const bool msk = masked(s);
-    // the stage's operands first (one LDS wait), then its 8 k-steps of MFMAs
+    // the stage's operands first (one LDS wait), then its DBK / 2 k-steps of MFMAs
     floatx4 a[DBK / 8][C::TM], b[DBK / 8][C::TN];
 #pragma unroll
     for (int u = 0; u < DBK / 8; ++u) {
@@ -470,13 +484,13 @@ __device__ __forceinline__ void dma_tile(const Dev& g, int64_t tile, char* ring)
 #pragma unroll
       for (int x = 0; x < C::TM; ++x) {
         const int row = wm * (BM / 2) + 32 * x + l32;
-        a[u][x] = *reinterpret_cast<const floatx4*>(sa + row * 64 + 16 * (c ^ ((row >> 2) & 3)));
+        a[u][x] = *reinterpret_cast<const floatx4*>(sa + row * KC_ROW + 16 * (c ^ kc_swz(row)));
       }
 #pragma unroll
       for (int y = 0; y < C::TN; ++y) {
         const int col = wn * (BN / 2) + 32 * y + l32;
         if (TB) {
-          b[u][y] = *reinterpret_cast<const floatx4*>(sb + col * 64 + 16 * (c ^ ((col >> 2) & 3)));
+          b[u][y] = *reinterpret_cast<const floatx4*>(sb + col * KC_ROW + 16 * (c ^ kc_swz(col)));
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -549,6 +563,15 @@ template <int BM, int BN, bool TB, int NS>
 __global__ void __launch_bounds__(256, 2) gemm_f32_dma(Dev g) {
   __shared__ __attribute__((aligned(1024))) char ring[NS * DCfg<BM, BN, TB>::STAGE];
   dma_tile<BM, BN, TB, NS>(g, blockIdx.x, ring);
+}
+
+// Two independent problems in one launch, as gemm_f32_pair, through the direct-to-LDS ring.
+template <int BM, int BN, bool TB1, bool TB2, int NS>
+__global__ void __launch_bounds__(256, 2) gemm_f32_dma_pair(Dev g1, int64_t tiles1, Dev g2) {
+  constexpr int S1 = DCfg<BM, BN, TB1>::STAGE, S2 = DCfg<BM, BN, TB2>::STAGE;
+  __shared__ __attribute__((aligned(1024))) char ring[NS * (S1 > S2 ? S1 : S2)];
+  if ((int64_t)blockIdx.x < tiles1) dma_tile<BM, BN, TB1, NS>(g1, blockIdx.x, ring);
+  else dma_tile<BM, BN, TB2, NS>(g2, (int64_t)blockIdx.x - tiles1, ring);
 }
 
 // ---------------------------------------------------------------------------------
@@ -687,6 +710,17 @@ hipError_t launch_dma(const Dev& g, bool tb, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int BM, int BN, int NS>
+hipError_t launch_dma_pair(const Dev& g1, bool tb1, const Dev& g2, bool tb2, hipStream_t s) {
+  const int64_t t1 = ceil_div(g1.M, BM) * ceil_div(g1.N, BN);
+  const int64_t grid = t1 + ceil_div(g2.M, BM) * ceil_div(g2.N, BN);
+  if (!tb1 && !tb2) hipLaunchKernelGGL((gemm_f32_dma_pair<BM, BN, false, false, NS>), dim3(grid), dim3(256), 0, s, g1, t1, g2);
+  else if (!tb1 && tb2) hipLaunchKernelGGL((gemm_f32_dma_pair<BM, BN, false, true, NS>), dim3(grid), dim3(256), 0, s, g1, t1, g2);
+  else if (tb1 && !tb2) hipLaunchKernelGGL((gemm_f32_dma_pair<BM, BN, true, false, NS>), dim3(grid), dim3(256), 0, s, g1, t1, g2);
+  else hipLaunchKernelGGL((gemm_f32_dma_pair<BM, BN, true, true, NS>), dim3(grid), dim3(256), 0, s, g1, t1, g2);
+  return hipGetLastError();
+}
+
 hipError_t launch_small(const Dev& g, bool tb, hipStream_t s) {
   const int64_t grid = ceil_div(g.M, SK_T) * ceil_div(g.N, SK_T);
   if (tb) hipLaunchKernelGGL((gemm_f32_small<true>), dim3(grid), dim3(256), 0, s, g);
@@ -731,6 +765,20 @@ int tile_order(const GemmArgs& a) {
   return 0;
 }
 
+// The direct-to-LDS kernels' preconditions: A row-major, 16-byte rows and chunks that do not
+// straddle an edge (K and, for a row-major B, N multiples of 4), and byte offsets inside a
+// 128-row tile below 2^31 (leading dimensions < 2^21).
+bool dma_ok(const GemmArgs& a, int vec) {
+  return vec && !a.transA && a.K % 4 == 0 && a.K >= 4 && (a.transB || a.N % 4 == 0) &&
+         a.M >= 64 && a.N >= 64 && a.lda < ((int64_t)1 << 21) && a.ldb < ((int64_t)1 << 21);
+}
+
+// Shortest K at which the direct-to-LDS kernel replaces the register-staged 128 x 128 one.
+// Measured on MI355X: from K = 1024 instead, no change; 64 x 64 direct-to-LDS tiles (four
+// workgroups per CU) from K = 256, 512 or 1024 in place of the register-staged 64 x 64
+// kernel, no change in prepare or quantize at d = 4096 ... 28672 (within 0.5 %).
+constexpr int64_t DMA128_MIN_K = 2048;
+
 Dev make_dev(const GemmArgs& a) {
   const int vec = aligned16(a.A) && aligned16(a.B) && !(a.lda % 4) && !(a.ldb % 4);
   return Dev{a.M, a.N, a.K, a.A, a.lda, a.triA, a.B, a.ldb, a.triB, a.C, a.ldc, a.triC, a.alpha,
@@ -754,6 +802,10 @@ hipError_t gemm_f32_pair(const GemmArgs& a1, const GemmArgs& a2, hipStream_t str
   const int64_t big = ceil_div(a1.M, 128) * ceil_div(a1.N, 128) + ceil_div(a2.M, 128) * ceil_div(a2.N, 128);
   const bool masked = (a1.triA || a1.triB || a1.triC || a2.triA || a2.triB || a2.triC) &&
                       big < 1024;
+  const bool dma = dma_ok(a1, g1.vec) && dma_ok(a2, g2.vec);
+  const int64_t k_min = a1.K < a2.K ? a1.K : a2.K;
+  if (!masked && big >= 512 && dma && k_min >= DMA128_MIN_K)
+    return launch_dma_pair<128, 128, DNS>(g1, a1.transB, g2, a2.transB, stream);
   if (!masked && big >= 512) return launch_pair<128, 128>(g1, a1.transB, g2, a2.transB, stream);
   return launch_pair<64, 64>(g1, a1.transB, g2, a2.transB, stream);
 }
@@ -780,15 +832,11 @@ hipError_t gemm_f32(const GemmArgs& a, hipStream_t stream, const char* prof_name
   // (one would wait for the longest), 64 x 64 tiles, longest first, let the dispatcher
   // balance the CUs; with many tiles per CU the larger tiles are more efficient.
   const bool masked = (a.triA || a.triB || a.triC) && big_tiles < 1024;
-  // direct-to-LDS path: A row-major, 16-byte rows and chunks that do not straddle an edge
-  // (byte offsets inside a 128-row tile stay below 2^31 for leading dimensions < 2^21)
-  const bool dma = vec && !a.transA && a.K % 4 == 0 && a.K >= 4 && (a.transB || a.N % 4 == 0) &&
-                   a.M >= 64 && a.N >= 64 && a.lda < ((int64_t)1 << 21) &&
-                   a.ldb < ((int64_t)1 << 21);
+  const bool dma = dma_ok(a, vec);
   // Measured on MI355X: 128 x 128 tiles pay off from about two per CU (4096 x 1024 x 1024:
   // 64 x 64 tiles 98 us, 128 x 128 120 us; 4096 x 2048 x 2048: all variants 330-345 us); the
   // direct-to-LDS kernel only for long K on large outputs.
-  if (!masked && dma && big_tiles >= 512 && a.K >= 2048)
+  if (!masked && dma && big_tiles >= 512 && a.K >= DMA128_MIN_K)
     return launch_dma<128, 128, DNS>(g, a.transB, stream);
   if (!masked && big_tiles >= 512) return launch<128, 128>(g, a.transA, a.transB, stream);
   return launch<64, 64>(g, a.transA, a.transB, stream);
