@@ -363,37 +363,55 @@ qgemm_dma(const _Float16* __restrict__ A, int64_t lda, int64_t M, const _Float16
 // The same product straight from the packed codes: dequantization inside the main loop (page
 // "量化", section AWQ: the weight-only kernel unpacks the codes in the GEMM's main loop, so the
 // weights cross HBM at b bits each).  Tiles, waves and the ring of three K stages are those
-// of qgemm_dma; a stage holds 128 rows of A (fp16, 16-byte copies) and the 256 rows of packed
-// codes of its 64 columns (8 b bytes per row, dword copies), so a stage of a 4-bit layer is
-// 24 KB instead of 48 KB.
+// of qgemm_dma; a stage of KD columns (64, or 128 for 4-bit codes in groups of 128 columns)
+// holds 128 rows of A (fp16, 16-byte copies) and the 256 rows of packed codes of its columns
+// (KD b / 8 bytes per row, dword copies): 24 KB for a 64-deep 4-bit stage instead of 48 KB,
+// 48 KB for a 128-deep one.  The deeper stage halves the barriers per column of K (measured
+// on MI355X at 2048 x 28672 x 8192: 1.44-1.47 ms against 1.50-1.54 ms).
 //
 // K order inside a stage: lane half h of an MFMA fragment (lanes 32 h .. 32 h + 31) takes the
-// stage's columns 32 h .. 32 h + 31 and step kk (0..3) the eight columns 32 h + 8 kk .. + 7.
-// The sum over a stage's 64 columns does not depend on which MFMA step and lane half a column
-// goes to, as long as A and B agree; with this order each lane's 32 codes of the stage are
-// contiguous (4 b bytes, one 16-byte LDS read for 4-bit codes) and are expanded in registers,
-// 8 per step: 1024 + c is the fp16 with bits 0x6400 | c, and one packed fp16 add of
-// -(1024 + z) gives c - z exactly.  Groups are whole stages (g % 64 == 0).
+// stage's columns (KD / 2) h .. (KD / 2) h + KD / 2 - 1 and step kk the eight columns
+// (KD / 2) h + 8 kk .. + 7.  The sum over a stage's columns does not depend on which MFMA step
+// and lane half a column goes to, as long as A and B agree; with this order each lane's codes
+// of the stage are contiguous (KD b / 16 bytes: one or two 16-byte LDS reads for 4-bit codes)
+// and are expanded in registers, 8 per step: 1024 + c is the fp16 with bits 0x6400 | c, and
+// one packed fp16 add of -(1024 + z) gives c - z exactly.  Groups are whole stages.
 //
-// LDS layout of the codes: row r's dwords of the stage at r * 2 b .. + 2 b - 1; for 4-bit codes
-// the two 16-byte halves of a row swap places in rows with bit 3 set, so the 16 lanes that one
-// LDS read cycle serves (rows r .. r + 15, the same half) fall in distinct banks.
+// LDS layout of the codes: row r's dwords of the stage at r * KD b / 32 ..; 4-bit rows are
+// permuted in 16-byte pieces (pk_pos) so that the 16 lanes that one LDS read cycle serves
+// (rows r .. r + 15, the same piece) fall in distinct banks.
 
-template <int BITS>
+template <int BITS, int KD>
 struct PackedCfg {
-  static constexpr int RD = 2 * BITS;                    // dwords per row and stage
+  static constexpr int A_ROW = KD * 2;                   // bytes of a row of A per stage
+  static constexpr int A_BYTES = DM * A_ROW;
+  static constexpr int SLOTS = KD / 8;                   // 16-byte slots per row of A
+  static constexpr int RD = KD * BITS / 32;              // dwords of codes per row and stage
   static constexpr int B_BYTES = DN * RD * 4;
-  static constexpr int STAGE = DA_BYTES + B_BYTES;
-  static constexpr int A_CPW = DA_BYTES / 1024 / DWAVES;   // 1 KB copies of A per wave: 2
-  static constexpr int B_CPW = DN * RD / 64 / DWAVES;      // 256 B copies of B per wave: BITS
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_CPW = A_BYTES / 1024 / DWAVES;  // 1 KB copies of A per wave: KD / 32
+  static constexpr int B_CPW = DN * RD / 64 / DWAVES;    // 256 B copies of B per wave
   static constexpr int CPW = A_CPW + B_CPW;
-  static constexpr int CHUNK = BITS;                      // dwords of codes per lane and stage
+  static constexpr int CHUNK = RD / 2;                   // dwords of codes per lane and stage
+  static_assert(KD == 64 || (KD == 128 && BITS == 4), "stage depths built");
 };
 
-// LDS dword position of global dword j of row r's stage segment (an involution)
-template <int BITS>
+// LDS slot of a row of A's 16-byte slot `slot`: 64-deep stages (128-byte rows, two to a bank
+// row) XOR by (row / 2) % 8, 128-deep stages (one 256-byte row per bank row) by row % 16, so
+// the 16 rows one read cycle serves fall in distinct banks (an involution)
+template <int KD>
+__device__ __forceinline__ int a_swz(int row, int slot) {
+  return KD == 64 ? slot ^ ((row >> 1) & 7) : slot ^ (row & 15);
+}
+
+// LDS dword position of global dword j of row r's stage segment (an involution).  4-bit rows
+// of a 64-deep stage are 32 bytes (8 to a bank row): the two 16-byte halves swap in rows with
+// bit 3 set; of a 128-deep stage 64 bytes (4 to a bank row): the four 16-byte quarters are
+// XORed with (row / 4) % 4.
+template <int BITS, int KD>
 __device__ __forceinline__ int pk_pos(int row, int j) {
-  if constexpr (BITS == 4) return j ^ (((row >> 3) & 1) << 2);
+  if constexpr (BITS == 4 && KD == 64) return j ^ (((row >> 3) & 1) << 2);
+  if constexpr (BITS == 4 && KD == 128) return j ^ (((row >> 2) & 3) << 2);
   return j;
 }
 
@@ -490,13 +508,13 @@ __device__ __forceinline__ half8 pk_slot_order(half8 a) {
   }
 }
 
-template <int BITS>
+template <int BITS, int KD>
 __global__ void __launch_bounds__(64 * DWAVES, 1)
 qgemm_packed(const _Float16* __restrict__ A, int64_t lda, int64_t M,
              const uint32_t* __restrict__ Q, const uint8_t* __restrict__ Z, int64_t N, int64_t K,
              const float* __restrict__ S, int64_t n_groups, int spg, float* __restrict__ C,
              int64_t ldc) {
-  using P = PackedCfg<BITS>;
+  using P = PackedCfg<BITS, KD>;
   __shared__ __attribute__((aligned(16))) char lds[DNST * P::STAGE];
   const int64_t tiles_m = (M + DM - 1) / DM;
   const int64_t tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
@@ -512,15 +530,15 @@ qgemm_packed(const _Float16* __restrict__ A, int64_t lda, int64_t M,
   const rsrc_t rb = make_rsrc(Q + n0 * wpr, rows_b * wpr * 4);
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)lds);
 
-  // copies of stage st: A copy q (< 16) covers rows 8 q .. 8 q + 7; B copy q covers the
-  // stage's LDS dwords 64 q .. 64 q + 63 of the code block
+  // copies of stage st: A copy q covers rows (1024 / A_ROW) q ..; B copy q covers the stage's
+  // LDS dwords 64 q .. 64 q + 63 of the code block
   auto issue = [&](int st, int slot) {
     const uint32_t sbase = lds0 + (uint32_t)(slot * P::STAGE);
 #pragma unroll
     for (int c = 0; c < P::A_CPW; ++c) {
       const int q = wave * P::A_CPW + c;
-      const int row = 8 * q + (lane >> 3);
-      const int voff = (int)((row * lda + st * DK + 8 * dswz(row, lane & 7)) * 2);
+      const int row = (1024 / P::A_ROW) * q + lane / P::SLOTS;
+      const int voff = (int)((row * lda + st * KD + 8 * a_swz<KD>(row, lane % P::SLOTS)) * 2);
       dcopy(ra, sbase + (uint32_t)q * 1024u, voff);
     }
 #pragma unroll
@@ -528,8 +546,8 @@ qgemm_packed(const _Float16* __restrict__ A, int64_t lda, int64_t M,
       const int q = wave * P::B_CPW + c;
       const int L = 64 * q + lane;
       const int row = L / P::RD, jl = L % P::RD;
-      const int voff = (int)((row * wpr + st * P::RD + pk_pos<BITS>(row, jl)) * 4);
-      dcopy4(rb, sbase + (uint32_t)DA_BYTES + (uint32_t)q * 256u, voff);
+      const int voff = (int)((row * wpr + st * P::RD + pk_pos<BITS, KD>(row, jl)) * 4);
+      dcopy4(rb, sbase + (uint32_t)P::A_BYTES + (uint32_t)q * 256u, voff);
     }
   };
 
@@ -556,7 +574,7 @@ qgemm_packed(const _Float16* __restrict__ A, int64_t lda, int64_t M,
   zero_points(0);
   int64_t grp = 0;
 
-  const int nst = (int)(K / DK);
+  const int nst = (int)(K / KD);
   issue(0, 0);
   if (nst > 1) issue(1, 1);
   int slot = 0, gstep = 0;          // ring slot of stage st, stage index within its group
@@ -572,10 +590,13 @@ qgemm_packed(const _Float16* __restrict__ A, int64_t lda, int64_t M,
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int row = wn * 64 + b * 32 + li;
-      const uint32_t* rb_l = reinterpret_cast<const uint32_t*>(sb + DA_BYTES) + row * P::RD;
+      const uint32_t* rb_l = reinterpret_cast<const uint32_t*>(sb + P::A_BYTES) + row * P::RD;
       if constexpr (BITS == 4) {
-        const uint4 v = *reinterpret_cast<const uint4*>(rb_l + pk_pos<4>(row, 4 * lh));
-        ch[b][0] = v.x; ch[b][1] = v.y; ch[b][2] = v.z; ch[b][3] = v.w;
+#pragma unroll
+        for (int j = 0; j < P::CHUNK; j += 4) {
+          const uint4 v = *reinterpret_cast<const uint4*>(rb_l + pk_pos<4, KD>(row, P::CHUNK * lh + j));
+          ch[b][j] = v.x; ch[b][j + 1] = v.y; ch[b][j + 2] = v.z; ch[b][j + 3] = v.w;
+        }
       } else if constexpr (BITS == 8) {
         const uint4 v = *reinterpret_cast<const uint4*>(rb_l + 8 * lh);
         const uint4 u = *reinterpret_cast<const uint4*>(rb_l + 8 * lh + 4);
@@ -590,13 +611,13 @@ qgemm_packed(const _Float16* __restrict__ A, int64_t lda, int64_t M,
       }
     }
     auto step = [&](int kk, auto first) {
-      const int lslot = 4 * lh + kk;
+      const int lslot = (KD / 16) * lh + kk;
       half8 af[2], bf[2];
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         const int row = wm * 64 + a * 32 + li;
         af[a] = pk_slot_order<BITS>(
-            *reinterpret_cast<const half8*>(sb + row * DROW + 16 * dswz(row, lslot)));
+            *reinterpret_cast<const half8*>(sb + row * P::A_ROW + 16 * a_swz<KD>(row, lslot)));
       }
 #pragma unroll
       for (int b = 0; b < 2; ++b) bf[b] = pk_expand<BITS>(ch[b], kk, nz[b], nz16[b]);
@@ -610,7 +631,7 @@ qgemm_packed(const _Float16* __restrict__ A, int64_t lda, int64_t M,
     if (fresh) step(0, std::true_type{});
     else step(0, std::false_type{});
 #pragma unroll
-    for (int kk = 1; kk < DK / 16; ++kk) step(kk, std::false_type{});
+    for (int kk = 1; kk < KD / 16; ++kk) step(kk, std::false_type{});
     slot = slot == DNST - 1 ? 0 : slot + 1;
     if (++gstep == spg) {                  // the group ends with this stage
       gstep = 0;
@@ -662,11 +683,18 @@ hipError_t qgemm_packed_f16(const _Float16* A, int64_t lda, int64_t M, const uin
   const int64_t tiles = ceil_div(M, DM) * ceil_div(N, DN);
   const dim3 grid((unsigned)tiles), block(64 * DWAVES);
   const int spg = (int)(g / DK);
+  // 4-bit codes with 128-column groups: 128-deep stages (48 KB, three in the ring), one
+  // group per stage and half the barriers per column of K
+  if (bits == 4 && K % 128 == 0 && g % 128 == 0) {
+    hipLaunchKernelGGL((qgemm_packed<4, 128>), grid, block, 0, s, A, lda, M, q, z, N, K, S, K / g,
+                       (int)(g / 128), C, ldc);
+    return hipGetLastError();
+  }
   switch (bits) {
-    case 2: hipLaunchKernelGGL(qgemm_packed<2>, grid, block, 0, s, A, lda, M, q, z, N, K, S, K / g, spg, C, ldc); break;
-    case 3: hipLaunchKernelGGL(qgemm_packed<3>, grid, block, 0, s, A, lda, M, q, z, N, K, S, K / g, spg, C, ldc); break;
-    case 4: hipLaunchKernelGGL(qgemm_packed<4>, grid, block, 0, s, A, lda, M, q, z, N, K, S, K / g, spg, C, ldc); break;
-    default: hipLaunchKernelGGL(qgemm_packed<8>, grid, block, 0, s, A, lda, M, q, z, N, K, S, K / g, spg, C, ldc); break;
+    case 2: hipLaunchKernelGGL((qgemm_packed<2, 64>), grid, block, 0, s, A, lda, M, q, z, N, K, S, K / g, spg, C, ldc); break;
+    case 3: hipLaunchKernelGGL((qgemm_packed<3, 64>), grid, block, 0, s, A, lda, M, q, z, N, K, S, K / g, spg, C, ldc); break;
+    case 4: hipLaunchKernelGGL((qgemm_packed<4, 64>), grid, block, 0, s, A, lda, M, q, z, N, K, S, K / g, spg, C, ldc); break;
+    default: hipLaunchKernelGGL((qgemm_packed<8, 64>), grid, block, 0, s, A, lda, M, q, z, N, K, S, K / g, spg, C, ldc); break;
   }
   return hipGetLastError();
 }

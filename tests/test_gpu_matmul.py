@@ -28,6 +28,9 @@ pytestmark = pytest.mark.gpu
     (2500, 300, 2048, 2, 128),    # INT2 read packed, ragged tiles both ways
     (129, 257, 640, 4, 0),        # per-channel INT4 read packed, one row past a tile each way
     (64, 512, 1024, 8, 256),      # INT8 read packed, groups of four stages
+    (200, 384, 1536, 4, 256),     # INT4 128-column stages, groups of two
+    (100, 300, 1600, 4, 64),      # INT4 with 64-column groups: 64-column stages
+    (70, 260, 192, 4, 0),         # per-channel INT4, d_col not a multiple of 128
 ])
 def test_dequant_matmul(n, d_row, d_col, bits, group):
     torch = _torch()
