@@ -202,15 +202,19 @@ __device__ __forceinline__ void quant_step(Row<B>& r, const float* gl, int c, in
   }
   const float x = r.w[A];
   const float v = div_by_scale(x, r.p) + r.p.z;
-  const float code = fminf(fmaxf(__builtin_rintf(v), 0.0f), (float)maxq);
+  // clip to [0, maxq] in one v_med3 (the same value as max then min for every input)
+  const float code = __builtin_amdgcn_fmed3f(__builtin_rintf(v), 0.0f, (float)maxq);
   const float wq = r.p.s * (code - r.p.z);
-  // d = w - w^ (e = d / G_qq is formed after the block; the stored G rows carry the 1/G_qq)
-  float dq = dpp<0x150 + O>(x - wq);  // row_newbcast: every lane takes the owner's d
-  if (Q >= width) dq = 0.0f;
-  if (c == O) {            // register selects, no memory traffic on the column chain
+  // d = w - w^ (e = d / G_qq is formed after the block; the stored G rows carry the 1/G_qq).
+  // Columns past `width` need no mask here: their weights are 0, so d is finite, and their
+  // staged coefficients and 1 / G_qq are 0, so d moves nothing and is never stored.
+  const float dq = dpp<0x150 + O>(x - wq);  // row_newbcast: every lane takes the owner's d
+  {                        // register selects, no memory traffic on the column chain
     constexpr int SH = 8 * (A % 4);
-    r.code[A / 4] = (r.code[A / 4] & ~(0xffu << SH)) | ((uint32_t)code << SH);
-    r.err[A] = dq;
+    const bool own = c == O;
+    const uint32_t cw = (r.code[A / 4] & ~(0xffu << SH)) | ((uint32_t)code << SH);
+    r.code[A / 4] = own ? cw : r.code[A / 4];
+    r.err[A] = own ? dq : r.err[A];
   }
 #pragma unroll
   for (int s = A; s < S; ++s) r.w[s] = fmaf(-dq, r.gc[s], r.w[s]);
