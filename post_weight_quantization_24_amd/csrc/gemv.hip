@@ -8,10 +8,12 @@
 //   * One wave per output row (a grid-stride loop over rows); lane l takes the runs of 32
 //     consecutive codes l, l + 64, ...  A run is exactly `bits` 32-bit words of the row, so
 //     every load is aligned and the lanes of a wave read consecutive bytes.  With g a
-//     multiple of 32 a run lies in one group: one scale and one zero per run.  For 4-bit codes
-//     all runs of a row (with their scales and zeros) are requested together, the next row's
-//     while the current one is reduced, and the first row's before the activations are
-//     staged.
+//     multiple of 32 a run lies in one group: one scale and one zero per run.  For 2- and
+//     4-bit codes with at most four runs per lane (d_col <= 8192) all runs of a row (with
+//     their scales and zeros) are requested together, the next row's while the current one is
+//     reduced, and the first row's before the activations are staged.
+//   * The grid is one round of resident workgroups (what the registers and the staged
+//     activations let fit on the chip), each wave looping over rows.
 //   * The activation rows are staged once per workgroup in LDS as fp16, piece-major.
 //   * INT4: the nibbles k and k + 4 of a word land in the two halves of
 //     (w >> 4k) & 0x000F000F; OR-ing 0x6400 into each half gives the fp16 values 1024 + q,
@@ -21,6 +23,8 @@
 //   * INT2, INT3, INT8: the codes are extracted from a 64-bit window of two words, converted
 //     to fp32 and accumulated with fp32 fused multiply-adds, one run after the other.
 //   * The 64 lane sums of a row are added by a butterfly, in a fixed order.
+
+#include <mutex>
 
 #include "gptq_internal.h"
 
@@ -82,6 +86,9 @@ __device__ __forceinline__ void load_runs(RowRuns<BITS, RPL>& rr, const uint32_t
       if constexpr (BITS == 4) {
         const uint4 v = *reinterpret_cast<const uint4*>(p);
         rr.w[i][0] = v.x; rr.w[i][1] = v.y; rr.w[i][2] = v.z; rr.w[i][3] = v.w;
+      } else if constexpr (BITS == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        rr.w[i][0] = v.x; rr.w[i][1] = v.y;
       } else if constexpr (BITS == 8) {
         const uint4 v0 = reinterpret_cast<const uint4*>(p)[0], v1 = reinterpret_cast<const uint4*>(p)[1];
         rr.w[i][0] = v0.x; rr.w[i][1] = v0.y; rr.w[i][2] = v0.z; rr.w[i][3] = v0.w;
@@ -214,9 +221,11 @@ dequant_matvec(const uint32_t* __restrict__ qw, const float* __restrict__ scales
   const int runs = dc / 32;
   const int64_t words = d_col * BITS / 32;          // per row
   int64_t r = (int64_t)blockIdx.x * MV_WAVES + (threadIdx.x >> 6);
-  // 4-bit codes with at most 4 runs per lane: whole rows in registers (prefetched); wider rows
-  // already give each lane several loads per row and take the codes run by run
-  constexpr bool PREFETCH = BITS == 4 && RPL <= 4;
+  // 2- and 4-bit codes with at most 4 runs per lane: whole rows in registers (prefetched).
+  // 8-bit codes and wider rows already give each lane several loads per row, and 3-bit codes
+  // are bound by their extraction (prefetched, they hold 91 VGPRs and ran 1-2 % slower on
+  // MI355X); they take the codes run by run.
+  constexpr bool PREFETCH = (BITS == 4 || BITS == 2) && RPL <= 4;
 
   // the first row's codes are requested before x is staged, so the two fetches overlap
   RowRuns<BITS, PREFETCH ? RPL : 1> rr;
@@ -276,16 +285,36 @@ template <int BITS, int RPL, int NB>
 hipError_t launch_nb(const uint32_t* qw, const float* scales, const uint8_t* zeros, int64_t d_row,
                      int64_t d_col, Grp g, const _Float16* x, int64_t ldx, float* y,
                      int64_t ldy, hipStream_t s) {
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(dequant_matvec<BITS, RPL, NB>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)MV_LDS);
-    if (e != hipSuccess) return e;
-    attr = true;
+  const void* fn = reinterpret_cast<const void*>(dequant_matvec<BITS, RPL, NB>);
+  // the dynamic LDS limit is raised once per device (callers on several threads share it)
+  static std::mutex mu;
+  static bool attr[64] = {};
+  static int cus[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    if (!attr[dev]) {
+      e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)MV_LDS);
+      if (e != hipSuccess) return e;
+      e = hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev);
+      if (e != hipSuccess) return e;
+      attr[dev] = true;
+    }
   }
-  const int64_t want = ceil_div(d_row, (int64_t)MV_WAVES);
-  const unsigned grid = (unsigned)(want < 1024 ? want : 1024);   // up to four per CU
   const size_t lds = (size_t)NB * d_col * sizeof(_Float16);
+  // One round of resident workgroups, each wave looping over rows: the grid is what fits on
+  // the chip at once (registers and the staged activations decide), so no partial second
+  // round of workgroups starts after the first (INT4 with 4 runs per lane holds 71 VGPRs:
+  // three 8-wave workgroups per CU, not four).
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, MV_THREADS, lds);
+  if (e != hipSuccess) return e;
+  const int64_t fit = (int64_t)(per_cu > 0 ? per_cu : 1) * (cus[dev] > 0 ? cus[dev] : 1);
+  const int64_t want = ceil_div(d_row, (int64_t)MV_WAVES);
+  const unsigned grid = (unsigned)(want < fit ? want : fit);
   hipLaunchKernelGGL((dequant_matvec<BITS, RPL, NB>), dim3(grid), dim3(MV_THREADS), lds, s, qw,
                      scales, zeros, d_row, d_col, g, x, ldx, y, ldy);
   return hipGetLastError();
