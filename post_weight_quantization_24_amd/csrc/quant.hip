@@ -37,6 +37,23 @@ convert_w(const void* __restrict__ W, int w_dtype, int64_t n, float* __restrict_
     Wc[i] = w_dtype == 0 ? (float)static_cast<const _Float16*>(W)[i]
                          : static_cast<const float*>(W)[i];
 }
+// The same in 16-byte pieces (W and Wc 16-byte aligned, n a multiple of 8): eight fp16 (two
+// pieces of four fp32) weights per thread and step, as two 16-byte stores.
+__global__ void __launch_bounds__(256)
+convert_w16(const void* __restrict__ W, int w_dtype, int64_t n, float* __restrict__ Wc) {
+  floatx4* out = reinterpret_cast<floatx4*>(Wc);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n / 8; i += (int64_t)gridDim.x * 256) {
+    if (w_dtype == 0) {
+      const half8 h = static_cast<const half8*>(W)[i];
+      out[2 * i] = floatx4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+      out[2 * i + 1] = floatx4{(float)h[4], (float)h[5], (float)h[6], (float)h[7]};
+    } else {
+      const floatx4* in = static_cast<const floatx4*>(W);
+      out[2 * i] = in[2 * i];
+      out[2 * i + 1] = in[2 * i + 1];
+    }
+  }
+}
 
 __global__ void __launch_bounds__(256) zero_f64(double* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
@@ -440,8 +457,15 @@ hipError_t quant_launch(const QuantArgs& a, void* ws, hipStream_t s) {
   const int64_t n_groups = a.d_col / g;
   {
     ProfScope ps("quant_convert", s);
-    const int64_t grid = ceil_div(n, 256) < 4096 ? ceil_div(n, 256) : 4096;
-    hipLaunchKernelGGL(convert_w, dim3((unsigned)grid), dim3(256), 0, s, a.W, a.w_dtype, n, Wc);
+    const bool vec = n % 8 == 0 &&
+                     ((reinterpret_cast<uintptr_t>(a.W) | reinterpret_cast<uintptr_t>(Wc)) & 15) == 0;
+    if (vec) {
+      const int64_t grid = ceil_div(n / 8, 256) < 8192 ? ceil_div(n / 8, 256) : 8192;
+      hipLaunchKernelGGL(convert_w16, dim3((unsigned)grid), dim3(256), 0, s, a.W, a.w_dtype, n, Wc);
+    } else {
+      const int64_t grid = ceil_div(n, 256) < 4096 ? ceil_div(n, 256) : 4096;
+      hipLaunchKernelGGL(convert_w, dim3((unsigned)grid), dim3(256), 0, s, a.W, a.w_dtype, n, Wc);
+    }
     if (a.err_sq_rows) {
       const int64_t gz = ceil_div(a.d_row, 256) < 1024 ? ceil_div(a.d_row, 256) : 1024;
       hipLaunchKernelGGL(zero_f64, dim3((unsigned)gz), dim3(256), 0, s, a.err_sq_rows, a.d_row);
