@@ -42,8 +42,18 @@ PrepWs carve(void* ws, int64_t d) {
 __global__ void __launch_bounds__(256)
 damp_lambda(const float* __restrict__ H, int64_t d, float frac, double* lambda, int* flag) {
   __shared__ double s[256];
+  // thread t adds H_ii for i = t, t + 256, ... in that order; eight loads go out before their
+  // additions (the order, and so the sum, is that of one load at a time)
   double acc = 0.0;
-  for (int64_t i = threadIdx.x; i < d; i += 256) acc += (double)H[i * d + i];
+  int64_t i = threadIdx.x;
+  for (; i + 7 * 256 < d; i += 8 * 256) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = H[(i + 256 * u) * d + i + 256 * u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += (double)v[u];
+  }
+  for (; i < d; i += 256) acc += (double)H[i * d + i];
   s[threadIdx.x] = acc;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
