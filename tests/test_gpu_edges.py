@@ -100,3 +100,33 @@ def test_exact_ties_round_half_even(sym):
     ties = np.abs(v - np.floor(v) - 0.5) == 0
     assert ties.sum() > d_row * d_col // 2
     assert np.all(r["codes"][ties] % 2 == 0)
+
+
+@pytest.mark.parametrize("wdt", ["f16", "f32"])
+def test_unaligned_weights(wdt):
+    """W one element past a 16-byte boundary takes the element-wise conversion to the float32
+    working copy (the aligned call converts in 16-byte pieces): codes, scales, zeros and the
+    row error sums equal the aligned call's bit for bit, and match the oracle."""
+    torch = _torch()
+    say("unaligned weights", wdt)
+    d_row, d_col = 40, 256
+    W = weight(946, "unal", d_row, d_col, wdt)
+    H = _workload_h(d_col, 4 * d_col, wid=947)
+    G32 = O.prepare_g(H, 0.01).astype(np.float32)
+    spec = G.Spec.make(4, 64, 0, 64, 0.01)
+    Gd = to_dev(G32)
+    Wa = to_dev(W)
+    flat = torch.empty(d_row * d_col + 1, dtype=Wa.dtype, device=Wa.device)
+    Wu = flat[1:].view(d_row, d_col)
+    Wu.copy_(Wa)
+    assert Wu.is_contiguous() and Wu.data_ptr() % 16 != 0
+    outs_a = G.quantize_layer(Wa, Gd, spec)
+    outs_u = G.quantize_layer(Wu, Gd, spec)
+    torch.cuda.synchronize()
+    for x, y in zip(outs_a, outs_u):
+        assert torch.equal(x, y)
+    st = compare(W, G32.astype(np.float64), dict(bits=4, group=64, sym=0),
+                 codes_of(outs_u[0], 4, d_col), outs_u[1].cpu().numpy(), outs_u[2].cpu().numpy(),
+                 H=H, block=64)
+    st.pop("fol")
+    say("stats", st)
