@@ -24,7 +24,9 @@
 //     to fp32 and accumulated with fp32 fused multiply-adds, one run after the other.
 //   * The 64 lane sums of a row are added by a butterfly, in a fixed order.
 
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "gptq_internal.h"
 
@@ -286,14 +288,18 @@ hipError_t launch_nb(const uint32_t* qw, const float* scales, const uint8_t* zer
                      int64_t d_col, Grp g, const _Float16* x, int64_t ldx, float* y,
                      int64_t ldy, hipStream_t s) {
   const void* fn = reinterpret_cast<const void*>(dequant_matvec<BITS, RPL, NB>);
-  // the dynamic LDS limit is raised once per device (callers on several threads share it)
+  const size_t lds = (size_t)NB * d_col * sizeof(_Float16);
+  // Per device, once (callers on several threads share it): the dynamic LDS limit is raised
+  // and the CU count read; per device and LDS size, once: the workgroups that fit on a CU.
   static std::mutex mu;
   static bool attr[64] = {};
   static int cus[64] = {};
+  static std::map<std::pair<int, size_t>, int> per_cu_of;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  int per_cu = 0;
   {
     std::lock_guard<std::mutex> lk(mu);
     if (!attr[dev]) {
@@ -303,15 +309,20 @@ hipError_t launch_nb(const uint32_t* qw, const float* scales, const uint8_t* zer
       if (e != hipSuccess) return e;
       attr[dev] = true;
     }
+    const auto key = std::make_pair(dev, lds);
+    const auto it = per_cu_of.find(key);
+    if (it != per_cu_of.end()) {
+      per_cu = it->second;
+    } else {
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, MV_THREADS, lds);
+      if (e != hipSuccess) return e;
+      per_cu_of[key] = per_cu;
+    }
   }
-  const size_t lds = (size_t)NB * d_col * sizeof(_Float16);
   // One round of resident workgroups, each wave looping over rows: the grid is what fits on
   // the chip at once (registers and the staged activations decide), so no partial second
   // round of workgroups starts after the first (INT4 with 4 runs per lane holds 71 VGPRs:
   // three 8-wave workgroups per CU, not four).
-  int per_cu = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, MV_THREADS, lds);
-  if (e != hipSuccess) return e;
   const int64_t fit = (int64_t)(per_cu > 0 ? per_cu : 1) * (cus[dev] > 0 ? cus[dev] : 1);
   const int64_t want = ceil_div(d_row, (int64_t)MV_WAVES);
   const unsigned grid = (unsigned)(want < fit ? want : fit);
