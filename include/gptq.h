@@ -166,12 +166,15 @@ int gptq_dequant_check(const uint32_t* qweight, const float* scales, const uint8
  * qweight, exactly as gptq_quantize_layer writes it (g = d_col when group = 0).
  *   qweight  [d_row x d_col*bits/32] uint32, 16-byte aligned; scales [d_row x d_col/g]
  *            fp32; zeros [d_row x d_col/g] uint8.
- *   x        [n x d_col] fp16 (x_dtype must be GPTQ_F16), row stride ldx >= d_col.
+ *   x        [n x d_col] fp16 (x_dtype must be GPTQ_F16), 4-byte aligned, row stride
+ *            ldx >= d_col (rows 16-byte aligned are staged 16 bytes at a time, others one
+ *            element at a time).
  *   y        [n x d_row] fp32 output, row stride ldy >= d_row.
  *   bits 2, 3, 4 or 8; group 0 (per-channel) or a multiple of 32 dividing d_col;
  *   d_col a multiple of 32 and at most 32768; 1 <= n <= 4096 (the rows are taken in groups
  *   whose fp16 copy fits 64 KB of LDS, at most 8 per launch).
- * Products are accumulated in fp32 (fp16 products of the exact integers q - z for 4 bits),
+ * Products are accumulated in fp32 (fp16 products of the exact integers q - z for 2 and 4
+ * bits),
  * one run of 32 codes at a time, then over runs in a fixed order: deterministic.
  * Errors: GPTQ_EINVAL for NULL pointers, shapes, strides or alignment; GPTQ_EHIP. */
 int gptq_dequant_matvec(const uint32_t* qweight, const float* scales, const uint8_t* zeros,

@@ -20,8 +20,11 @@
 //     and subtracting 1024 + z leaves q - z exactly (|q - z| < 16).  v_dot2_f32_f16 then
 //     multiplies the pair with (x_k, x_k+4) and accumulates in fp32, so x is staged in that
 //     pair order.  Per run the fp32 dot of (q - z) and x is scaled once by s.
-//   * INT2, INT3, INT8: the codes are extracted from a 64-bit window of two words, converted
-//     to fp32 and accumulated with fp32 fused multiply-adds, one run after the other.
+//   * INT2: the same with the codes j and j + 8 of a word: (w >> 8s) & (0x00030003 << 2t)
+//     ORed with 0x6400 is the pair 1024 + 4^t q, one packed fma by 4^-t with -(1024 4^-t + z)
+//     leaves q - z exactly, and v_dot2_f32_f16 takes (x_j, x_j+8), staged in that order.
+//   * INT3, INT8: the codes are extracted from a 64-bit window of two words, converted to
+//     fp32 and accumulated with fp32 fused multiply-adds, one run after the other.
 //   * The 64 lane sums of a row are added by a butterfly, in a fixed order.
 
 #include <map>
@@ -106,16 +109,44 @@ __device__ __forceinline__ void load_runs(RowRuns<BITS, RPL>& rr, const uint32_t
   }
 }
 
-// Activation rows to LDS (pair order for 4-bit codes).  16-byte pieces of 8 columns, four
-// loads per thread in flight before the stores; the pair order (x_k, x_k+4) of a piece is a
-// shuffle of its four dwords.  Piece p of run k is stored at (p * runs + k) * 16 bytes, so the
-// 64 lanes of a wave (runs k .. k + 63) read consecutive 16-byte slots: no bank conflicts.
-// Unaligned rows fall back to one element at a time.
-template <bool PAIRS>
+// Activation rows to LDS, in the pair order of the code expansion: for 4-bit codes
+// (x_k, x_k+4) within each 8-column piece, for 2-bit codes (x_j, x_j+8) within each
+// 16-column block (two pieces), else natural.  16-byte pieces of 8 columns, four loads per
+// thread in flight before the stores; the pair orders are shuffles of the pieces' dwords.
+// Piece p of run k is stored at (p * runs + k) * 16 bytes, so the 64 lanes of a wave (runs
+// k .. k + 63) read consecutive 16-byte slots: no bank conflicts.  Unaligned rows fall back to
+// one element at a time.
+__device__ __forceinline__ int pos2(int c) {   // 2-bit pair order inside a 32-column run
+  const int r = c & 31, i = r >> 4, j = r & 15, kk = j & 7;
+  return 16 * i + 8 * (kk >> 2) + 2 * (kk & 3) + (j >> 3);
+}
+template <int MODE>
 __device__ __forceinline__ void stage_x(_Float16* xs, const _Float16* __restrict__ x, int64_t ldx,
                                         int nb, int dc) {
+  constexpr bool PAIRS = MODE == 4;
   const bool vec = ((reinterpret_cast<uintptr_t>(x) | (uintptr_t)(ldx * 2)) & 15) == 0;
-  if (vec) {
+  if (MODE == 2 && vec) {
+    // two pieces (a 16-column block) per thread and step: (x_j, x_j+8) for j = 0..3 into the
+    // first output piece, j = 4..7 into the second
+    const int per_row = dc / 16, blocks = nb * per_row;
+    for (int i = threadIdx.x; i < blocks; i += MV_THREADS) {
+      const int b = i / per_row, c16 = i - b * per_row;
+      const uint4 v0 = *reinterpret_cast<const uint4*>(x + b * ldx + 16 * c16);
+      const uint4 v1 = *reinterpret_cast<const uint4*>(x + b * ldx + 16 * c16 + 8);
+      uint4 o0, o1;
+      o0.x = (v0.x & 0xffffu) | (v1.x << 16);
+      o0.y = (v0.x >> 16) | (v1.x & 0xffff0000u);
+      o0.z = (v0.y & 0xffffu) | (v1.y << 16);
+      o0.w = (v0.y >> 16) | (v1.y & 0xffff0000u);
+      o1.x = (v0.z & 0xffffu) | (v1.z << 16);
+      o1.y = (v0.z >> 16) | (v1.z & 0xffff0000u);
+      o1.z = (v0.w & 0xffffu) | (v1.w << 16);
+      o1.w = (v0.w >> 16) | (v1.w & 0xffff0000u);
+      const int k = c16 >> 1, p = 2 * (c16 & 1);          // run, first output piece
+      *reinterpret_cast<uint4*>(xs + b * dc + 8 * (p * (dc / 32) + k)) = o0;
+      *reinterpret_cast<uint4*>(xs + b * dc + 8 * ((p + 1) * (dc / 32) + k)) = o1;
+    }
+  } else if (vec) {
     const int per_row = dc / 8, pieces = nb * per_row;
     for (int i0 = threadIdx.x; i0 < pieces; i0 += 4 * MV_THREADS) {
       uint4 v[4];
@@ -147,8 +178,9 @@ __device__ __forceinline__ void stage_x(_Float16* xs, const _Float16* __restrict
   } else {
     for (int i = threadIdx.x; i < nb * dc; i += MV_THREADS) {
       const int b = i / dc, c = i - b * dc;
-      const int k = c >> 5, p = (c >> 3) & 3, e = PAIRS ? pos4(c) & 7 : c & 7;
-      xs[b * dc + 8 * (p * (dc / 32) + k) + e] = x[b * ldx + c];
+      const int k = c >> 5;
+      const int q = MODE == 2 ? pos2(c) : (c & 24) + (PAIRS ? pos4(c) & 7 : c & 7);
+      xs[b * dc + 8 * ((q >> 3) * (dc / 32) + k) + (q & 7)] = x[b * ldx + c];
     }
   }
 }
@@ -181,6 +213,46 @@ __device__ __forceinline__ void run_dot(const uint32_t (&w)[BITS], int z, const 
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           part[b] = __builtin_amdgcn_fdot2(q[kk], __builtin_bit_cast(half2v, xa[kk]), part[b],
+                                           false);
+      }
+    }
+  } else if constexpr (BITS == 2) {
+    // word i holds columns 16 i .. 16 i + 15 of the run.  For kk = 4 s + t, the codes kk and
+    // kk + 8 sit in bits 8 s + 2 t (+ 16) of the word: masked in place and ORed with
+    // 0x6400 they are the fp16 values 1024 + 4^t c, and one packed fma by 4^-t with
+    // -(1024 4^-t + z) leaves c - z exactly (all values are small integers times powers of 2).
+    const uint32_t magic = 0x64006400u;
+    half2v scl[4], off[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const _Float16 sc = (_Float16)(1.0f / (float)(1 << (2 * t)));
+      const _Float16 of = (_Float16)(-(1024.0f / (float)(1 << (2 * t))) - (float)z);
+      scl[t] = half2v{sc, sc};
+      off[t] = half2v{of, of};
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      half2v q[8];
+#pragma unroll
+      for (int s8 = 0; s8 < 2; ++s8) {
+        const uint32_t ws = w[i] >> (8 * s8);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          uint32_t h;
+          __asm__("v_and_or_b32 %0, %1, %2, %3"
+                  : "=v"(h)
+                  : "v"(ws), "s"(0x00030003u << (2 * t)), "v"(magic));
+          q[4 * s8 + t] = __builtin_bit_cast(half2v, h) * scl[t] + off[t];
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const uint4 xa = *reinterpret_cast<const uint4*>(xs + b * dc + 8 * ((2 * i) * (dc / 32) + k));
+        const uint4 xb = *reinterpret_cast<const uint4*>(xs + b * dc + 8 * ((2 * i + 1) * (dc / 32) + k));
+        const uint32_t xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+          part[b] = __builtin_amdgcn_fdot2(q[kk], __builtin_bit_cast(half2v, xv[kk]), part[b],
                                            false);
       }
     }
@@ -235,7 +307,7 @@ dequant_matvec(const uint32_t* __restrict__ qw, const float* __restrict__ scales
     if (r < d_row)
       load_runs<BITS, RPL>(rr, qw + r * words, scales + r * gp.n_groups, zeros + r * gp.n_groups, gp,
                            runs, lane);
-  stage_x<BITS == 4>(xs, x, ldx, NB, dc);
+  stage_x<BITS == 4 ? 4 : BITS == 2 ? 2 : 0>(xs, x, ldx, NB, dc);
   __syncthreads();
 
   for (; r < d_row; r += n_waves) {

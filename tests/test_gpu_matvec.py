@@ -71,6 +71,7 @@ CASES = [  # d_row, d_col, bits, group, n
     (77, 256, 4, 128, 1), (300, 4096, 4, 128, 1), (64, 4096, 4, 0, 3), (129, 1024, 4, 32, 8),
     (100, 1024, 3, 128, 2), (65, 2048, 3, 0, 1), (90, 512, 2, 32, 4), (33, 4096, 2, 256, 1),
     (70, 1024, 8, 128, 5), (17, 32768, 4, 128, 1), (40, 2048, 4, 128, 11),
+    (50, 8192, 2, 0, 2), (21, 16384, 2, 64, 1), (30, 2048, 2, 128, 11),   # 2-bit pair order
 ]
 
 
@@ -114,3 +115,28 @@ def test_matvec_fullsize_70b_gate():
     words, scales, zeros = packed_layer(rng, d_row, d_col, bits, group)
     rows = np.sort(rng.choice(d_row, 64, replace=False))
     check(words, scales, zeros, acts(rng, 1, d_col), bits, group, d_col, rows=rows)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_matvec_unaligned_activations(bits):
+    """Activation rows two columns past a 16-byte boundary (the 4-byte alignment the entry
+    point asks for) with a row stride of d_col + 2: the activations are staged one element at
+    a time, in each width's pair order, and the result equals the aligned call's."""
+    torch = _torch()
+    say("dequant_matvec unaligned x", bits)
+    rng = np.random.default_rng(1100 + bits)
+    d_row, d_col, group, n = 45, 1024, 128, 3
+    words, scales, zeros = packed_layer(rng, d_row, d_col, bits, group)
+    x = acts(rng, n, d_col)
+    dev = "cuda:0"
+    full = torch.zeros((n, d_col + 2), dtype=torch.float16, device=dev)
+    full[:, 2:] = torch.from_numpy(x).to(dev)
+    xd = full[:, 2:]
+    assert xd.stride(0) == d_col + 2 and xd.data_ptr() % 16 != 0 and xd.data_ptr() % 4 == 0
+    qw = torch.from_numpy(words.view(np.int32)).to(dev)
+    y = G.dequant_matvec(qw, torch.from_numpy(scales).to(dev), torch.from_numpy(zeros).to(dev),
+                         xd, bits, group, d_col)
+    torch.cuda.synchronize()
+    y_al = run_gpu(words, scales, zeros, x, bits, group, d_col)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), y_al)
+    check(words, scales, zeros, x, bits, group, d_col)
