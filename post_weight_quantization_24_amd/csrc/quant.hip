@@ -219,7 +219,8 @@ __device__ __forceinline__ void quant_step(Row<B>& r, const float* gl, int c, in
   }
   const float x = r.w[A];
   const float v = div_by_scale(x, r.p) + r.p.z;
-  // clip to [0, maxq] in one v_med3 (the same value as max then min for every input)
+  // clip to [0, maxq] in one v_med3 (the same value as max then min for every finite or
+  // infinite v; finite weights never give a NaN here)
   const float code = __builtin_amdgcn_fmed3f(__builtin_rintf(v), 0.0f, (float)maxq);
   const float wq = r.p.s * (code - r.p.z);
   // d = w - w^ (e = d / G_qq is formed after the block; the stored G rows carry the 1/G_qq).
