@@ -14,8 +14,8 @@
 // With beta = 1 the C tile is loaded into the accumulators before the K loop and alpha
 // (+1 or -1) is folded into op(A) as it is staged, so the epilogue is a plain store.
 // Products with at most one 64 x 64 tile per CU go to a short-K kernel instead (32 x 32
-// tiles, K split over the four waves of a workgroup); long-K products with many 128 x 128
-// tiles to a direct-to-LDS variant.
+// tiles, K split over the four waves of a workgroup); long-K products and product pairs
+// with many 128 x 128 tiles to a direct-to-LDS variant.
 
 #include "gptq_internal.h"
 
