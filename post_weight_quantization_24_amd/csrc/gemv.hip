@@ -23,8 +23,12 @@
 //   * INT2: the same with the codes j and j + 8 of a word: (w >> 8s) & (0x00030003 << 2t)
 //     ORed with 0x6400 is the pair 1024 + 4^t q, one packed fma by 4^-t with -(1024 4^-t + z)
 //     leaves q - z exactly, and v_dot2_f32_f16 takes (x_j, x_j+8), staged in that order.
-//   * INT3, INT8: the codes are extracted from a 64-bit window of two words, converted to
-//     fp32 and accumulated with fp32 fused multiply-adds, one run after the other.
+//   * INT3: codes i and i + 16 of a run lie 48 bits apart, so the low halves of
+//     (w >> 3i) over the run's low 64 bits and over its high 64 bits hold them at bits 0 and
+//     16; masked and ORed with 0x6400 they are the pair 1024 + q, the packed subtract of
+//     1024 + z leaves q - z, and v_dot2_f32_f16 takes (x_i, x_i+16), staged in that order.
+//   * INT8: the codes are extracted from a 64-bit window of two words, converted to fp32 and
+//     accumulated with fp32 fused multiply-adds, one run after the other.
 //   * The 64 lane sums of a row are added by a butterfly, in a fixed order.
 
 #include <map>
@@ -120,12 +124,40 @@ __device__ __forceinline__ int pos2(int c) {   // 2-bit pair order inside a 32-c
   const int r = c & 31, i = r >> 4, j = r & 15, kk = j & 7;
   return 16 * i + 8 * (kk >> 2) + 2 * (kk & 3) + (j >> 3);
 }
+__device__ __forceinline__ int pos3(int c) {   // 3-bit pair order: (x_i, x_i+16) of a run
+  const int r = c & 31, i = r & 15;
+  return 8 * (i >> 2) + 2 * (i & 3) + (r >> 4);
+}
 template <int MODE>
 __device__ __forceinline__ void stage_x(_Float16* xs, const _Float16* __restrict__ x, int64_t ldx,
                                         int nb, int dc) {
   constexpr bool PAIRS = MODE == 4;
   const bool vec = ((reinterpret_cast<uintptr_t>(x) | (uintptr_t)(ldx * 2)) & 15) == 0;
-  if (MODE == 2 && vec) {
+  if (MODE == 3 && vec) {
+    // a whole run (four pieces) per thread and step: (x_i, x_i+16) for i = 0..15, four pairs
+    // per output piece
+    const int per_row = dc / 32, runs_all = nb * per_row;
+    for (int i = threadIdx.x; i < runs_all; i += MV_THREADS) {
+      const int b = i / per_row, k = i - b * per_row;
+      const uint4* src = reinterpret_cast<const uint4*>(x + b * ldx + 32 * k);
+      const uint4 v[4] = {src[0], src[1], src[2], src[3]};
+#pragma unroll
+      for (int hp = 0; hp < 2; ++hp) {     // pieces hp and hp + 2 pair up
+        const uint4 lo = v[hp], hi = v[hp + 2];
+        uint4 o0, o1;
+        o0.x = (lo.x & 0xffffu) | (hi.x << 16);
+        o0.y = (lo.x >> 16) | (hi.x & 0xffff0000u);
+        o0.z = (lo.y & 0xffffu) | (hi.y << 16);
+        o0.w = (lo.y >> 16) | (hi.y & 0xffff0000u);
+        o1.x = (lo.z & 0xffffu) | (hi.z << 16);
+        o1.y = (lo.z >> 16) | (hi.z & 0xffff0000u);
+        o1.z = (lo.w & 0xffffu) | (hi.w << 16);
+        o1.w = (lo.w >> 16) | (hi.w & 0xffff0000u);
+        *reinterpret_cast<uint4*>(xs + b * dc + 8 * ((2 * hp) * (dc / 32) + k)) = o0;
+        *reinterpret_cast<uint4*>(xs + b * dc + 8 * ((2 * hp + 1) * (dc / 32) + k)) = o1;
+      }
+    }
+  } else if (MODE == 2 && vec) {
     // two pieces (a 16-column block) per thread and step: (x_j, x_j+8) for j = 0..3 into the
     // first output piece, j = 4..7 into the second
     const int per_row = dc / 16, blocks = nb * per_row;
@@ -179,7 +211,7 @@ __device__ __forceinline__ void stage_x(_Float16* xs, const _Float16* __restrict
     for (int i = threadIdx.x; i < nb * dc; i += MV_THREADS) {
       const int b = i / dc, c = i - b * dc;
       const int k = c >> 5;
-      const int q = MODE == 2 ? pos2(c) : (c & 24) + (PAIRS ? pos4(c) & 7 : c & 7);
+      const int q = MODE == 2 ? pos2(c) : MODE == 3 ? pos3(c) : (c & 24) + (PAIRS ? pos4(c) & 7 : c & 7);
       xs[b * dc + 8 * ((q >> 3) * (dc / 32) + k) + (q & 7)] = x[b * ldx + c];
     }
   }
@@ -256,6 +288,42 @@ __device__ __forceinline__ void run_dot(const uint32_t (&w)[BITS], int z, const 
                                            false);
       }
     }
+  } else if constexpr (BITS == 3) {
+    // code i of the run at bit 3 i of (w2:w1:w0); codes i and i + 16 are 48 bits apart, so
+    // (w >> 3 i) of the low 64 bits has code i at bit 0 and (w >> 3 i) of the high 64 bits
+    // code i + 16 at bit 16: their low and high halves, masked and ORed with 0x6400, are the
+    // fp16 pair (1024 + q_i, 1024 + q_i+16), and one packed subtract of 1024 + z leaves
+    // q - z exactly.
+    const _Float16 zh = (_Float16)(1024 + z);
+    const half2v zz = {zh, zh};
+    const uint32_t magic = 0x64006400u;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {            // output piece p: pairs i = 4 p .. 4 p + 3
+      half2v q[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * p + e, sh = 3 * i;
+        const uint32_t lo = sh < 32 ? __builtin_amdgcn_alignbit(w[1], w[0], (uint32_t)sh)
+                                    : __builtin_amdgcn_alignbit(w[2], w[1], (uint32_t)(sh - 32));
+        const uint32_t hi = sh < 32 ? __builtin_amdgcn_alignbit(w[2], w[1], (uint32_t)sh)
+                                    : w[2] >> (sh - 32);
+        const uint32_t both = __builtin_amdgcn_perm(hi, lo, 0x07060100u);   // lo 16 | hi 16
+        uint32_t t;
+        __asm__("v_and_or_b32 %0, %1, %2, %3"
+                : "=v"(t)
+                : "v"(both), "s"(0x00070007u), "v"(magic));
+        q[e] = __builtin_bit_cast(half2v, t) - zz;
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const uint4 xv = *reinterpret_cast<const uint4*>(xs + b * dc + 8 * (p * (dc / 32) + k));
+        const uint32_t xa[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          part[b] = __builtin_amdgcn_fdot2(q[e], __builtin_bit_cast(half2v, xa[e]), part[b],
+                                           false);
+      }
+    }
   } else {
     const float zf = (float)z;
 #pragma unroll
@@ -296,9 +364,9 @@ dequant_matvec(const uint32_t* __restrict__ qw, const float* __restrict__ scales
   const int64_t words = d_col * BITS / 32;          // per row
   int64_t r = (int64_t)blockIdx.x * MV_WAVES + (threadIdx.x >> 6);
   // 2- and 4-bit codes with at most 4 runs per lane: whole rows in registers (prefetched).
-  // 8-bit codes and wider rows already give each lane several loads per row, and 3-bit codes
-  // are bound by their extraction (prefetched, they hold 91 VGPRs and ran 1-2 % slower on
-  // MI355X); they take the codes run by run.
+  // 8-bit codes and wider rows already give each lane several loads per row; 3-bit codes,
+  // prefetched (71-145 VGPRs), measured -1 % to +4 % on MI355X.  They take the codes run by
+  // run.
   constexpr bool PREFETCH = (BITS == 4 || BITS == 2) && RPL <= 4;
 
   // the first row's codes are requested before x is staged, so the two fetches overlap
@@ -307,7 +375,7 @@ dequant_matvec(const uint32_t* __restrict__ qw, const float* __restrict__ scales
     if (r < d_row)
       load_runs<BITS, RPL>(rr, qw + r * words, scales + r * gp.n_groups, zeros + r * gp.n_groups, gp,
                            runs, lane);
-  stage_x<BITS == 4 ? 4 : BITS == 2 ? 2 : 0>(xs, x, ldx, NB, dc);
+  stage_x<BITS == 8 ? 0 : BITS>(xs, x, ldx, NB, dc);
   __syncthreads();
 
   for (; r < d_row; r += n_waves) {
