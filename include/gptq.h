@@ -118,6 +118,38 @@ size_t gptq_prepare_workspace_size(int64_t d);
 int gptq_prepare_hinv(const float* H, float* G, int64_t d, float damp_frac, void* ws,
                       size_t ws_bytes, int64_t* info, void* stream);
 
+/* Inspection of the blocked schedule that gptq_prepare_hinv runs on diagonal blocks of
+ * 1024 to 2048 columns (host only: no HIP call, usable without a GPU).  The same factor
+ * as above, taken in 128-column blocks from the bottom right (page "量化", GPTQ, Cholesky
+ * reformulation, in blocked form): per block a leaf factor G_kk = U_kk^-1, the panel
+ * U[0:c_k, k] = A[0:c_k, k] G_kk^T into a scratch matrix, the update of the next block's
+ * column, and the trailing update; the blocks of G above the diagonal from a binary tree
+ * over the blocks.  All on the caller's stream: each leaf is one workgroup of a launch
+ * whose other workgroups run the previous block's trailing update and tiles of the tree
+ * products whose inputs are complete.
+ *   n, ld  block size and leading dimension of the matrix it sits in (ld >= n).
+ *   out    NULL or cap records of GPTQ_PLAN_FIELDS int64 each.  Record 0: number of
+ *          128-blocks, 0, U-scratch floats, tree-scratch floats, number of launches.
+ *          Then one record per launch in stream order:
+ *            [0] kind (0 a leaf and/or tile ranges of up to six products in one launch,
+ *                1 one whole product), [1] number of products, [2] 0,
+ *            [3] leaf offset on the diagonal, [4] leaf size (0: no leaf),
+ *            [5 + 21 j .. 26 + 21 j) product j: M, N, K, then for A, B and C the buffer
+ *                (0 the matrix, offsets from the block's corner; 1 the U scratch, n x n;
+ *                2 the tree scratch), offset and leading dimension, followed by transA,
+ *                triA (after A), transB, triB (after B), triC (after C), alpha, beta, and
+ *                the range [t0, t1) of its 64 x 64 tiles in the product's tile order (tile
+ *                t is tile row t / tiles_per_row, column t % tiles_per_row; by columns
+ *                instead when triB = 2, by columns from the last when triB = 1, by rows
+ *                from the last when triA = 2).
+ *          C = alpha op(A) op(B) + beta C with op(X) = X^T when transX; triA/triB 1 (2):
+ *          op(X) is upper (lower) triangular, entries outside are zero and never read;
+ *          triC 1: only entries on or above the diagonal of C are written.
+ * Returns the number of records needed (written when cap suffices); GPTQ_EINVAL for n < 1,
+ * n > 65536 or ld < n. */
+#define GPTQ_PLAN_FIELDS 160
+int64_t gptq_prepare_plan(int64_t n, int64_t ld, int64_t* out, int64_t cap);
+
 /* ---------------------------------------------------------------- column solve (a4-a7)
  * Quantizes W with GPTQ given G from gptq_prepare_hinv (page "量化", GPTQ: fixed order,
  * OBS compensation through G, blocks of spec->block columns with a lazy batch update).

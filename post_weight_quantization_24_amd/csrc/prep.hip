@@ -10,12 +10,21 @@
 //     G11 = factor(A11)                     (recursion)
 //     G12 = -G11 Q                          (written over A12)
 // All products run on the fp32 MFMA GEMM; blocks of at most 128 are factored and
-// inverted by one workgroup in LDS.  Everything happens in the upper triangle of G;
-// the strictly lower triangle is zeroed at the end.
+// inverted by one workgroup in LDS.  Blocks of 1024 to 2048 columns are factored by the
+// blocked schedule of prep_plan.h instead, whose launches run each one-workgroup leaf
+// beside the previous block's trailing update and the tree products that form G's
+// off-diagonal blocks.  Everything happens in the upper triangle of G; the strictly lower
+// triangle is zeroed at the end.
 
 #include <climits>
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
 
+#include "gemm_tile.h"
 #include "gptq_internal.h"
+#include "prep_plan.h"
 
 namespace gptq {
 
@@ -290,11 +299,17 @@ __device__ __forceinline__ void put_unit(float* slot, const floatx4& v, int rho,
   }
 }
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-leaf_factor_invert(float* __restrict__ A, int64_t ld, int64_t off, int n, int* flag) {
-  __shared__ float slot[NSLOT * SLOT];
-  __shared__ float ubuf[(NLB - 1) * SLOT];
-  __shared__ int bad_at;
+struct LeafSmem {
+  float slot[NSLOT * SLOT];
+  float ubuf[(NLB - 1) * SLOT];
+  int bad_at;
+};
+
+__device__ __forceinline__ void leaf_body(float* __restrict__ A, int64_t ld, int64_t off, int n,
+                                          int* flag, LeafSmem& sm) {
+  float* slot = sm.slot;
+  float* ubuf = sm.ubuf;
+  int& bad_at = sm.bad_at;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   float* blk = A + off * ld + off;
@@ -401,6 +416,69 @@ leaf_factor_invert(float* __restrict__ A, int64_t ld, int64_t off, int n, int* f
   if (tid == 0 && bad_at != INT_MAX) atomicMin(flag, (int)(off + bad_at) + 1);
 }
 
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+leaf_factor_invert(float* __restrict__ A, int64_t ld, int64_t off, int n, int* flag) {
+  __shared__ LeafSmem sm;
+  leaf_body(A, ld, off, n, flag, sm);
+}
+
+// One launch of the blocked schedule: workgroup 0 factors a leaf (when leaf_n > 0) while
+// the others run 64 x 64 tiles of up to FUSED_TASKS independent products (tile ranges, with
+// the tile code of the GEMM launches), all sharing one LDS allocation.
+struct FusedArgs {
+  float* A;
+  int64_t ld, leaf_off;
+  int* flag;
+  int leaf_n, ntask;
+  Dev g[plan::FUSED_TASKS];
+  int64_t t0[plan::FUSED_TASKS], cnt[plan::FUSED_TASKS];
+  int tb[plan::FUSED_TASKS];
+};
+union FusedSmem {
+  LeafSmem leaf;
+  Smem<64, 64> gm;
+};
+
+__global__ void __launch_bounds__(256, 2) prep_fused(FusedArgs a) {
+  __shared__ __attribute__((aligned(16))) FusedSmem sm;
+  int64_t b = blockIdx.x;
+  if (a.leaf_n > 0) {
+    if (b == 0) {
+      leaf_body(a.A, a.ld, a.leaf_off, a.leaf_n, a.flag, sm.leaf);
+      return;
+    }
+    --b;
+  }
+  for (int i = 0; i < a.ntask; ++i) {
+    if (b < a.cnt[i]) {
+      const int64_t t = a.t0[i] + b;
+      if (a.tb[i]) gemm_tile<64, 64, false, true>(a.g[i], t, sm.gm);
+      else gemm_tile<64, 64, false, false>(a.g[i], t, sm.gm);
+      return;
+    }
+    b -= a.cnt[i];
+  }
+}
+
+
+// Blocks factored by the blocked schedule (prep_plan.h) instead of the recursion below.
+// Measured on MI355X (prepare at d = 1024 ... 11008): from 1024 it beats the recursion; up to
+// 2048 its trailing updates and tree products fit beside the leaves, while at 4096 the
+// early trailing updates (rank 128 over a 3840-square triangle) outlast the leaf and the
+// recursion's one split into two 2048 halves with large products is faster.
+constexpr int64_t BLK_MIN = 1024, BLK_MAX = 2048;
+bool blocked(int64_t n) { return n > NB && n >= BLK_MIN && n <= BLK_MAX; }
+
+// Plans by (n, ld), built once (the ones a process uses are few).
+const plan::Plan& plan_of(int64_t n, int64_t ld) {
+  static std::mutex mu;
+  static std::map<std::pair<int64_t, int64_t>, plan::Plan> cache;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find({n, ld});
+  if (it == cache.end()) it = cache.emplace(std::make_pair(n, ld), plan::blocked_plan(n, ld)).first;
+  return it->second;
+}
+
 // Split of an n-block: the leading m columns (a multiple of the leaf size) and the rest.
 int64_t split_of(int64_t n) {
   int64_t m = (n / 2) / NB * NB;
@@ -408,19 +486,74 @@ int64_t split_of(int64_t n) {
 }
 // Floats of the Q stack needed by factor_rec on an n-block (see below).
 int64_t q_stack(int64_t n) {
-  if (n <= NB) return 0;
+  if (n <= NB || blocked(n)) return 0;
   const int64_t m = split_of(n), r = n - m;
   const int64_t own = align_up((size_t)(m * r), 64);
   const int64_t right = q_stack(r), left = own + q_stack(m);
   return right > left ? right : left;
+}
+// Floats of the blocked schedule's scratch (U and the tree's Q blocks) for the largest
+// block the recursion hands to it; the blocked calls run one after another.
+int64_t blk_floats(int64_t n) {
+  if (n <= NB) return 0;
+  if (blocked(n)) {
+    const plan::Plan& p = plan_of(n, n);
+    return align_up((size_t)p.panel_floats, 64) + p.q_floats;
+  }
+  const int64_t m = split_of(n), a = blk_floats(m), b = blk_floats(n - m);
+  return a > b ? a : b;
+}
+
+GemmArgs args_of(const plan::Gemm& g, float* const* bufs) {
+  return GemmArgs{g.M, g.N, g.K, bufs[g.A.buf] + g.A.off, g.A.ld, g.transA, g.triA,
+                  bufs[g.B.buf] + g.B.off, g.B.ld, g.transB, g.triB,
+                  bufs[g.C.buf] + g.C.off, g.C.ld, g.triC, g.alpha, g.beta};
+}
+
+// The n-block at (off, off) by the blocked schedule, on the caller's stream.
+hipError_t factor_blocked(float* A, int64_t ld, int64_t off, int64_t n, float* scratch, int* flag,
+                          hipStream_t s) {
+  if (ld >= ((int64_t)1 << 24)) return hipErrorInvalidValue;   // 32-bit in-tile offsets
+  const plan::Plan& p = plan_of(n, ld);
+  float* bufs[3] = {A + off * ld + off, scratch, scratch + align_up((size_t)p.panel_floats, 64)};
+  for (const plan::Op& o : p.ops) {
+    hipError_t e;
+    if (o.kind == plan::GEMM) {
+      e = gemm_f32(args_of(o.t[0].g, bufs), s, "prep_gemm");
+    } else {
+      FusedArgs fa{};
+      fa.A = A;
+      fa.ld = ld;
+      fa.leaf_off = off + o.off;
+      fa.flag = flag;
+      fa.leaf_n = (int)o.n;
+      fa.ntask = (int)o.t.size();
+      int64_t grid = o.n > 0 ? 1 : 0;
+      for (int i = 0; i < fa.ntask; ++i) {
+        const plan::Task& t = o.t[i];
+        const GemmArgs ga = args_of(t.g, bufs);
+        fa.g[i] = make_dev(ga);
+        fa.t0[i] = t.t0;
+        fa.cnt[i] = t.t1 - t.t0;
+        fa.tb[i] = ga.transB;
+        grid += fa.cnt[i];
+      }
+      ProfScope ps(o.n > 0 ? "prep_leaf" : "prep_gemm", s);
+      hipLaunchKernelGGL(prep_fused, dim3((unsigned)grid), dim3(256), 0, s, fa);
+      e = hipGetLastError();
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // P (m x r) is scratch shared by all nodes (it is dead once Q and the Schur update are
 // formed); Q = P G22 must survive the recursion on A11, so each node takes its Q from a
 // stack above the ones of its ancestors.
 hipError_t factor_rec(float* A, int64_t ld, int64_t off, int64_t n, float* P, float* qstack,
-                      int* flag, hipStream_t s) {
+                      float* blk, int* flag, hipStream_t s) {
   hipError_t e;
+  if (blocked(n)) return factor_blocked(A, ld, off, n, blk, flag, s);
   if (n <= NB) {
     ProfScope ps("prep_leaf", s);
     hipLaunchKernelGGL(leaf_factor_invert, dim3(1), dim3(256), 0, s, A, ld, off, (int)n, flag);
@@ -432,7 +565,7 @@ hipError_t factor_rec(float* A, int64_t ld, int64_t off, int64_t n, float* P, fl
   float* A22 = A + (off + m) * ld + off + m;
   float* Q = qstack;
 
-  if ((e = factor_rec(A, ld, off + m, r, P, qstack, flag, s)) != hipSuccess) return e;
+  if ((e = factor_rec(A, ld, off + m, r, P, qstack, blk, flag, s)) != hipSuccess) return e;
   // P = A12 G22^T   (op(B)[k][j] = G22[j][k], zero for k < j)
   if ((e = gemm_f32({m, r, r, A12, ld, 0, 0, A22, ld, 1, 2, P, r, 0, 1.0f, 0.0f}, s,
                     "prep_gemm")) != hipSuccess)
@@ -442,7 +575,7 @@ hipError_t factor_rec(float* A, int64_t ld, int64_t off, int64_t n, float* P, fl
                          {m, m, r, P, r, 0, 0, P, r, 1, 0, A11, ld, 1, -1.0f, 1.0f}, s,
                          "prep_gemm")) != hipSuccess)
     return e;
-  if ((e = factor_rec(A, ld, off, m, P, qstack + align_up((size_t)(m * r), 64), flag, s)) !=
+  if ((e = factor_rec(A, ld, off, m, P, qstack + align_up((size_t)(m * r), 64), blk, flag, s)) !=
       hipSuccess)
     return e;
   // G12 = -G11 Q   (G11 upper: zero for k < i), straight into A12
@@ -451,9 +584,14 @@ hipError_t factor_rec(float* A, int64_t ld, int64_t off, int64_t n, float* P, fl
 
 }  // namespace
 
+// Floats of the recursion's P scratch (its largest product), none when the whole matrix
+// goes to the blocked schedule.
+int64_t p_floats(int64_t d) { return d > NB && !blocked(d) ? split_of(d) * (d - split_of(d)) : 0; }
+
 size_t prepare_ws_bytes(int64_t d) {
-  const int64_t p = d > NB ? split_of(d) * (d - split_of(d)) : 0;   // largest P
-  return 256 + (align_up((size_t)p, 64) + (size_t)q_stack(d) + 64) * sizeof(float);
+  const int64_t p = p_floats(d);
+  return 256 + (align_up((size_t)p, 64) + align_up((size_t)q_stack(d), 64) +
+                (size_t)blk_floats(d) + 64) * sizeof(float);
 }
 
 int* prepare_flag_ptr(void* ws, int64_t d) { return carve(ws, d).flag; }
@@ -474,10 +612,9 @@ hipError_t prepare_launch(const float* H, float* G, int64_t d, float damp_frac, 
       hipLaunchKernelGGL(copy_damp, rows_grid(d, d), dim3(256), 0, stream, H, G, d, w.lambda);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int64_t p = d > NB ? split_of(d) * (d - split_of(d)) : 0;
-  if ((e = factor_rec(G, d, 0, d, w.tmp, w.tmp + align_up((size_t)p, 64), w.flag, stream)) !=
-      hipSuccess)
-    return e;
+  float* qs = w.tmp + align_up((size_t)p_floats(d), 64);
+  float* blk = qs + align_up((size_t)q_stack(d), 64);
+  if ((e = factor_rec(G, d, 0, d, w.tmp, qs, blk, w.flag, stream)) != hipSuccess) return e;
   if (vec4)
     hipLaunchKernelGGL(zero_lower4, dim3((unsigned)(d < 16384 ? d : 16384)), dim3(256), 0, stream, G,
                        d);

@@ -49,10 +49,18 @@ def test_prepare_validation(lib):
     f = lib.gptq_prepare_hinv
     ws = lib.gptq_prepare_workspace_size(64)
     assert ws >= 256                      # lambda and the pivot flag
-    # blocks above the leaf size need the P scratch (2048 x 2048 floats at d = 4096) and the
-    # stack of Q blocks (one per level of the left spine)
-    assert lib.gptq_prepare_workspace_size(4096) >= (2048 * 2048 + 2048 * 2048) * 4
-    assert lib.gptq_prepare_workspace_size(4096) < 4096 * 4096 * 4
+    # d = 512: the recursion's P scratch (256 x 256 floats) and its stack of Q blocks
+    assert lib.gptq_prepare_workspace_size(512) >= (256 * 256 + 256 * 256) * 4
+    assert lib.gptq_prepare_workspace_size(512) < 512 * 512 * 4
+    # d = 2048: the blocked schedule's U scratch (d x d floats) and the tree's Q blocks (as
+    # the plan reports), no recursion scratch
+    head, _ = G.prepare_plan(2048)
+    assert head[2] == 2048 * 2048 and 2048 * 2048 // 4 <= head[3] < 2048 * 2048 // 2
+    ws2 = lib.gptq_prepare_workspace_size(2048)
+    need = (head[2] + head[3]) * 4
+    assert need <= ws2 < need + 4096
+    # d = 4096: one recursion split (P of 2048 x 2048) above two blocked halves
+    assert lib.gptq_prepare_workspace_size(4096) >= (2048 * 2048 * 2) * 4 + ws2 - 4096
     assert f(FAKE, FAKE, 0, 0.01, FAKE, ws, None, None) == G.EINVAL
     assert f(None, FAKE, 64, 0.01, FAKE, ws, None, None) == G.EINVAL
     assert f(FAKE, FAKE, 64, -0.5, FAKE, ws, None, None) == G.EINVAL

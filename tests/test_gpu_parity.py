@@ -109,8 +109,9 @@ def _workload_h(d, n_tok, wid=93, outlier_frac=0.0):
 
 
 # d = 99 and 130 (not multiples of 4) take the element-wise copy and clear; the others the
-# 16-byte ones
-@pytest.mark.parametrize("d", [99, 100, 128, 130, 200, 320, 1024])
+# 16-byte ones.  d = 1024, 1100 (a ragged last block) and 2048 take the blocked schedule,
+# the others the recursion.
+@pytest.mark.parametrize("d", [99, 100, 128, 130, 200, 320, 1024, 1100, 2048])
 def test_prepare_against_oracle(d):
     torch = _torch()
     say("prepare", d)
@@ -125,10 +126,10 @@ def test_prepare_against_oracle(d):
     assert np.abs(Gg.T @ Gg @ Hd - np.eye(d)).max() < 1e-3
 
 
-def test_prepare_outlier_channels_and_in_place():
+@pytest.mark.parametrize("d", [512, 1536])
+def test_prepare_outlier_channels_and_in_place(d):
     torch = _torch()
-    say("prepare outliers in place")
-    d = 512
+    say("prepare outliers in place", d)
     H = _workload_h(d, 8 * d, wid=94, outlier_frac=0.01).astype(np.float32)
     Hd_dev = to_dev(H)
     Gd = G.prepare_hinv(Hd_dev, G=Hd_dev, damp_frac=0.01)   # in place
