@@ -126,17 +126,22 @@ int gptq_prepare_hinv(const float* H, float* G, int64_t d, float damp_frac, void
  * column, and the trailing update; the blocks of G above the diagonal from a binary tree
  * over the blocks.  All on the caller's stream: each leaf is one workgroup of a launch
  * whose other workgroups run the previous block's trailing update and tiles of the tree
- * products whose inputs are complete.
- *   n, ld  block size and leading dimension of the matrix it sits in (ld >= n).
+ * products whose inputs are complete.  When the block is the left half of a recursion node
+ * with an r-column right half, the schedule also forms that node's Q = P G22 (P = A12 G22^T,
+ * n x r; G22 the factored r-block right below and right of the block) in K chunks of 512
+ * that start on G22's diagonal, beside the leaves.
+ *   n, ld  block size and leading dimension of the matrix it sits in (ld >= n + r).
+ *   r      columns of the node's right half whose Q comes along (0: none).
  *   out    NULL or cap records of GPTQ_PLAN_FIELDS int64 each.  Record 0: number of
- *          128-blocks, 0, U-scratch floats, tree-scratch floats, number of launches.
+ *          128-blocks, r, U-scratch floats, tree-scratch floats, number of launches.
  *          Then one record per launch in stream order:
  *            [0] kind (0 a leaf and/or tile ranges of up to six products in one launch,
  *                1 one whole product), [1] number of products, [2] 0,
  *            [3] leaf offset on the diagonal, [4] leaf size (0: no leaf),
  *            [5 + 21 j .. 26 + 21 j) product j: M, N, K, then for A, B and C the buffer
  *                (0 the matrix, offsets from the block's corner; 1 the U scratch, n x n;
- *                2 the tree scratch), offset and leading dimension, followed by transA,
+ *                2 the tree scratch; 3 the node's P and 4 its Q, n x r with leading
+ *                dimension r), offset and leading dimension, followed by transA,
  *                triA (after A), transB, triB (after B), triC (after C), alpha, beta, and
  *                the range [t0, t1) of its 64 x 64 tiles in the product's tile order (tile
  *                t is tile row t / tiles_per_row, column t % tiles_per_row; by columns
@@ -146,9 +151,9 @@ int gptq_prepare_hinv(const float* H, float* G, int64_t d, float damp_frac, void
  *          op(X) is upper (lower) triangular, entries outside are zero and never read;
  *          triC 1: only entries on or above the diagonal of C are written.
  * Returns the number of records needed (written when cap suffices); GPTQ_EINVAL for n < 1,
- * n > 65536 or ld < n. */
+ * n > 65536, r < 0, r > 65536 or ld < n + r. */
 #define GPTQ_PLAN_FIELDS 160
-int64_t gptq_prepare_plan(int64_t n, int64_t ld, int64_t* out, int64_t cap);
+int64_t gptq_prepare_plan(int64_t n, int64_t ld, int64_t r, int64_t* out, int64_t cap);
 
 /* ---------------------------------------------------------------- column solve (a4-a7)
  * Quantizes W with GPTQ given G from gptq_prepare_hinv (page "量化", GPTQ: fixed order,

@@ -223,20 +223,22 @@ int gptq_prepare_hinv(const float* H, float* G, int64_t d, float damp_frac, void
   return GPTQ_OK;
 }
 
-int64_t gptq_prepare_plan(int64_t n, int64_t ld, int64_t* out, int64_t cap) {
+int64_t gptq_prepare_plan(int64_t n, int64_t ld, int64_t r, int64_t* out, int64_t cap) {
   g_last_error.clear();
-  if (n < 1 || n > (int64_t)1 << 16 || ld < n) return fail(GPTQ_EINVAL, "n or ld out of range");
-  const gptq::plan::Plan p = gptq::plan::blocked_plan(n, ld);
+  if (n < 1 || n > (int64_t)1 << 16 || r < 0 || r > (int64_t)1 << 16 || ld < n + r)
+    return fail(GPTQ_EINVAL, "n, r or ld out of range");
+  const gptq::plan::Plan p = gptq::plan::blocked_plan(n, ld, r);
   const int64_t need = (int64_t)p.ops.size() + 1;
   if (!out || cap < need) return need;
   static_assert(5 + 21 * gptq::plan::FUSED_TASKS <= GPTQ_PLAN_FIELDS, "record too short");
-  int64_t* r = out;
-  for (int i = 0; i < GPTQ_PLAN_FIELDS; ++i) r[i] = 0;
-  r[0] = p.nb; r[2] = p.panel_floats; r[3] = p.q_floats; r[4] = (int64_t)p.ops.size();
+  int64_t* rec = out;
+  for (int i = 0; i < GPTQ_PLAN_FIELDS; ++i) rec[i] = 0;
+  rec[0] = p.nb; rec[1] = p.r; rec[2] = p.panel_floats; rec[3] = p.q_floats;
+  rec[4] = (int64_t)p.ops.size();
   for (const gptq::plan::Op& o : p.ops) {
-    r += GPTQ_PLAN_FIELDS;
-    for (int i = 0; i < GPTQ_PLAN_FIELDS; ++i) r[i] = 0;
-    r[0] = o.kind; r[1] = (int64_t)o.t.size(); r[3] = o.off; r[4] = o.n;
+    rec += GPTQ_PLAN_FIELDS;
+    for (int i = 0; i < GPTQ_PLAN_FIELDS; ++i) rec[i] = 0;
+    rec[0] = o.kind; rec[1] = (int64_t)o.t.size(); rec[3] = o.off; rec[4] = o.n;
     for (size_t j = 0; j < o.t.size(); ++j) {
       const gptq::plan::Task& t = o.t[j];
       const gptq::plan::Gemm& g = t.g;
@@ -244,7 +246,7 @@ int64_t gptq_prepare_plan(int64_t n, int64_t ld, int64_t* out, int64_t cap) {
                              g.B.buf, g.B.off, g.B.ld, g.transB, g.triB,
                              g.C.buf, g.C.off, g.C.ld, g.triC,
                              (int64_t)g.alpha, (int64_t)g.beta, t.t0, t.t1};
-      for (int i = 0; i < 21; ++i) r[5 + 21 * j + i] = v[i];
+      for (int i = 0; i < 21; ++i) rec[5 + 21 * j + i] = v[i];
     }
   }
   return need;

@@ -19,6 +19,7 @@
 #include <climits>
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <utility>
 #include <vector>
 
@@ -469,13 +470,14 @@ __global__ void __launch_bounds__(256, 2) prep_fused(FusedArgs a) {
 constexpr int64_t BLK_MIN = 1024, BLK_MAX = 2048;
 bool blocked(int64_t n) { return n > NB && n >= BLK_MIN && n <= BLK_MAX; }
 
-// Plans by (n, ld), built once (the ones a process uses are few).
-const plan::Plan& plan_of(int64_t n, int64_t ld) {
+// Plans by (n, ld, r), built once (the ones a process uses are few).
+const plan::Plan& plan_of(int64_t n, int64_t ld, int64_t r) {
   static std::mutex mu;
-  static std::map<std::pair<int64_t, int64_t>, plan::Plan> cache;
+  static std::map<std::tuple<int64_t, int64_t, int64_t>, plan::Plan> cache;
   std::lock_guard<std::mutex> lk(mu);
-  auto it = cache.find({n, ld});
-  if (it == cache.end()) it = cache.emplace(std::make_pair(n, ld), plan::blocked_plan(n, ld)).first;
+  const auto key = std::make_tuple(n, ld, r);
+  auto it = cache.find(key);
+  if (it == cache.end()) it = cache.emplace(key, plan::blocked_plan(n, ld, r)).first;
   return it->second;
 }
 
@@ -497,7 +499,7 @@ int64_t q_stack(int64_t n) {
 int64_t blk_floats(int64_t n) {
   if (n <= NB) return 0;
   if (blocked(n)) {
-    const plan::Plan& p = plan_of(n, n);
+    const plan::Plan& p = plan_of(n, n, 0);
     return align_up((size_t)p.panel_floats, 64) + p.q_floats;
   }
   const int64_t m = split_of(n), a = blk_floats(m), b = blk_floats(n - m);
@@ -510,12 +512,15 @@ GemmArgs args_of(const plan::Gemm& g, float* const* bufs) {
                   bufs[g.C.buf] + g.C.off, g.C.ld, g.triC, g.alpha, g.beta};
 }
 
-// The n-block at (off, off) by the blocked schedule, on the caller's stream.
+// The n-block at (off, off) by the blocked schedule, on the caller's stream; with r > 0 it
+// also forms the enclosing node's Q = P G22 (P, Q: n x r, G22 the r-block at (off + n,
+// off + n)).
 hipError_t factor_blocked(float* A, int64_t ld, int64_t off, int64_t n, float* scratch, int* flag,
-                          hipStream_t s) {
+                          hipStream_t s, float* P = nullptr, float* Q = nullptr, int64_t r = 0) {
   if (ld >= ((int64_t)1 << 24)) return hipErrorInvalidValue;   // 32-bit in-tile offsets
-  const plan::Plan& p = plan_of(n, ld);
-  float* bufs[3] = {A + off * ld + off, scratch, scratch + align_up((size_t)p.panel_floats, 64)};
+  const plan::Plan& p = plan_of(n, ld, r);
+  float* bufs[5] = {A + off * ld + off, scratch, scratch + align_up((size_t)p.panel_floats, 64),
+                    P, Q};
   for (const plan::Op& o : p.ops) {
     hipError_t e;
     if (o.kind == plan::GEMM) {
@@ -570,6 +575,14 @@ hipError_t factor_rec(float* A, int64_t ld, int64_t off, int64_t n, float* P, fl
   if ((e = gemm_f32({m, r, r, A12, ld, 0, 0, A22, ld, 1, 2, P, r, 0, 1.0f, 0.0f}, s,
                     "prep_gemm")) != hipSuccess)
     return e;
+  if (blocked(m)) {
+    // A11 <- A11 - P P^T (upper triangle); Q = P G22 runs beside A11's leaves
+    if ((e = gemm_f32({m, m, r, P, r, 0, 0, P, r, 1, 0, A11, ld, 1, -1.0f, 1.0f}, s,
+                      "prep_gemm")) != hipSuccess)
+      return e;
+    if ((e = factor_blocked(A, ld, off, m, blk, flag, s, P, Q, r)) != hipSuccess) return e;
+    return gemm_f32({m, r, m, A11, ld, 0, 1, Q, r, 0, 0, A12, ld, 0, -1.0f, 0.0f}, s, "prep_gemm");
+  }
   // Q = P G22 (G22 upper: zero for k > j), and A11 <- A11 - P P^T (upper triangle)
   if ((e = gemm_f32_pair({m, r, r, P, r, 0, 0, A22, ld, 0, 1, Q, r, 0, 1.0f, 0.0f},
                          {m, m, r, P, r, 0, 0, P, r, 1, 0, A11, ld, 1, -1.0f, 1.0f}, s,

@@ -20,13 +20,23 @@
 // entries.  Every product has the operand forms of the recursion's (op(A) = A; op(B) = B or
 // B^T; triangular masks on G blocks; an upper-only output).
 //
-// Operations are described by offsets into three buffers: 0 the matrix (upper triangle A,
+// When the block is the left half A11 of a recursion node whose right half (r columns) is
+// already factored, the schedule can also carry that node's Q = P G22 (P = A12 G22^T, n x r;
+// G22 the r x r upper factor right below and right of the block), which the node needs only
+// after this block: its tiles run beside the leaves, split along K into chunks that start on
+// G22's diagonal, Q[:, k0:r] += P[:, k0:k0+kc] G22[k0:k0+kc, k0:r] (upper again from its own
+// corner), each chunk in a later launch than the one before.
+//
+// Operations are described by offsets into five buffers: 0 the matrix (upper triangle A,
 // then G; row-major with leading dimension ld, offsets from the block's top-left corner),
 // 1 the n x n scratch matrix of U's blocks above the diagonal (leading dimension n), 2 the
-// Q scratch (one region per tree node).
+// Q scratch of the tree (one region per tree node), 3 the node's P and 4 its Q (n x r,
+// leading dimension r).
 #pragma once
 
 #include <stdint.h>
+
+#include <climits>
 
 #include <vector>
 
@@ -45,6 +55,8 @@ struct Gemm {
 };
 constexpr int FUSED_TASKS = 6;          // products beside the leaf in one launch
 constexpr int64_t TREE_BUDGET = 1 << 19; // tree tiles x K per launch (512 tiles of K 1024)
+constexpr int64_t NODE_Q_K = 512;        // k per chunk of the parent node's Q
+constexpr int64_t NODE_Q_TILES = 192;    // its tiles per launch beside a leaf
 
 enum Kind { FUSED = 0, GEMM = 1 };
 struct Task {
@@ -59,7 +71,7 @@ struct Op {
 };
 
 struct Plan {
-  int64_t n, ld, nb;
+  int64_t n, ld, nb, r;   // r: columns of the parent node's Q carried along (0: none)
   int64_t panel_floats; // buffer 1 (n * n)
   int64_t q_floats;     // buffer 2
   std::vector<Op> ops;
@@ -85,10 +97,11 @@ inline void build_tree(int64_t n, int64_t a, int64_t b, std::vector<Node>& out, 
 
 inline Mat matA(int64_t ld, int64_t r, int64_t c) { return Mat{0, r * ld + c, ld}; }
 
-inline Plan blocked_plan(int64_t n, int64_t ld) {
+inline Plan blocked_plan(int64_t n, int64_t ld, int64_t r = 0) {
   Plan p;
   p.n = n;
   p.ld = ld;
+  p.r = r;
   p.nb = (n + PB - 1) / PB;
   const int64_t nb = p.nb;
   auto col = [&](int64_t k) { return col_of(n, k); };
@@ -98,6 +111,8 @@ inline Plan blocked_plan(int64_t n, int64_t ld) {
   build_tree(n, 0, nb, tree, q_total);
   p.q_floats = q_total;
   const int nt = (int)tree.size();
+  const int nq = r > 0 ? (int)((r + NODE_Q_K - 1) / NODE_Q_K) : 0;   // chunks of the node's Q
+  const int ns = 2 * nt + nq;                                        // steps off the chain
 
   // Positions of the chain's launches: for k = nb-1 .. 0 the fused launch of leaf k, then
   // (k > 0) the panel and the column update.
@@ -107,9 +122,9 @@ inline Plan blocked_plan(int64_t n, int64_t ld) {
   // Tree steps: 2 t (Q of node t) and 2 t + 1 (G block of node t), each done in chunks of
   // 64 x 64 tiles.  A step may start in a launch after the one that completes its inputs:
   // the leaves and panels of its half (`after`) and the G steps of the nodes inside that half.
-  std::vector<Gemm> step(2 * nt);
-  std::vector<std::vector<int>> deps(2 * nt);
-  std::vector<int64_t> after(2 * nt, -1);
+  std::vector<Gemm> step(ns);
+  std::vector<std::vector<int>> deps(ns);
+  std::vector<int64_t> after(ns, -1);
   for (int t = 0; t < nt; ++t) {
     const Node& x = tree[t];
     const int64_t ca = col(x.a), cm = col(x.m), cb = col(x.b);
@@ -137,12 +152,24 @@ inline Plan blocked_plan(int64_t n, int64_t ld) {
       if (y.a >= x.a && y.b <= x.m) deps[2 * t + 1].push_back(2 * u + 1);
     }
   }
-  std::vector<int64_t> done_at(2 * nt, -1);           // launch holding each step's last tiles
-  std::vector<int64_t> next_tile(2 * nt, 0);
-  int64_t n_left = 2 * nt;
+  for (int c = 0; c < nq; ++c) {                     // the node's Q, chunk by chunk
+    const int64_t k0 = c * NODE_Q_K, kc = r - k0 < NODE_Q_K ? r - k0 : NODE_Q_K;
+    Gemm q{};
+    q.M = n; q.N = r - k0; q.K = kc;                   // Q[:, k0:r] (+)= P[:, k0:k0+kc] G22[..]
+    q.A = Mat{3, k0, r};
+    q.B = matA(ld, n + k0, n + k0); q.triB = 1;        // G22 from its diagonal entry (k0, k0)
+    q.C = Mat{4, k0, r};
+    q.alpha = 1.0f; q.beta = c == 0 ? 0.0f : 1.0f;
+    step[2 * nt + c] = q;
+    if (c > 0) deps[2 * nt + c].push_back(2 * nt + c - 1);
+  }
+  std::vector<int64_t> done_at(ns, -1);               // launch holding each step's last tiles
+  std::vector<int64_t> next_tile(ns, 0);
+  int64_t n_left = ns;
   // Tiles of ready steps for the launch at `pos`, within the budget (none: no limit).
   auto take_ready = [&](int64_t pos, int room, int64_t budget, std::vector<Task>& out) {
-    for (int s = 0; s < 2 * nt && room > 0; ++s) {
+    int64_t q_room = budget > 0 ? NODE_Q_TILES : INT64_MAX;   // the node's Q: a budget of its own
+    for (int s = 0; s < ns && room > 0; ++s) {
       if (done_at[s] >= 0 || after[s] >= pos) continue;
       bool ok = true;
       for (int d : deps[s])
@@ -151,7 +178,11 @@ inline Plan blocked_plan(int64_t n, int64_t ld) {
       const int64_t total = tiles_of(step[s]);
       const int64_t k = step[s].K > 0 ? step[s].K : 1;
       int64_t cnt = total - next_tile[s];
-      if (budget > 0) {
+      if (s >= 2 * nt) {
+        if (q_room <= 0) continue;
+        if (cnt > q_room) cnt = q_room;
+        q_room -= cnt;
+      } else if (budget > 0) {
         const int64_t fit = budget / k;
         if (fit <= 0) break;
         if (cnt > fit) cnt = fit;

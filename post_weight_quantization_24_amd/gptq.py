@@ -47,7 +47,7 @@ _SIGS = {
     "gptq_hessian_accumulate": ([_vp, _i64, _vp, _int, _i64, _i64, _vp, _sz, _vp], _int),
     "gptq_prepare_workspace_size": ([_i64], _sz),
     "gptq_prepare_hinv": ([_vp, _vp, _i64, _f32, _vp, _sz, ctypes.POINTER(_i64), _vp], _int),
-    "gptq_prepare_plan": ([_i64, _i64, ctypes.POINTER(_i64), _i64], _i64),
+    "gptq_prepare_plan": ([_i64, _i64, _i64, ctypes.POINTER(_i64), _i64], _i64),
     "gptq_quantize_workspace_size": ([_i64, _i64, ctypes.POINTER(Spec)], _sz),
     "gptq_quantize_layer": ([_vp, _int, _i64, _i64, _vp, ctypes.POINTER(Spec), _vp, _vp, _vp, _vp,
                              _vp, _sz, _vp], _int),
@@ -221,16 +221,17 @@ def prepare_hinv(H, G=None, damp_frac=0.01, ws=None, check=True, stream=None):
 PLAN_FIELDS = 160
 
 
-def prepare_plan(n: int, ld: Optional[int] = None):
-    """The blocked inverse-factor schedule for an n-block (host only, no GPU): returns
-    (header, ops) as int64 arrays of PLAN_FIELDS columns, laid out as include/gptq.h says."""
+def prepare_plan(n: int, ld: Optional[int] = None, r: int = 0):
+    """The blocked inverse-factor schedule for an n-block (host only, no GPU), carrying the
+    enclosing node's Q for an r-column right half when r > 0: returns (header, ops) as int64
+    arrays of PLAN_FIELDS columns, laid out as include/gptq.h says."""
     import numpy as np
-    ld = n if ld is None else ld
-    need = lib().gptq_prepare_plan(n, ld, None, 0)
+    ld = n + r if ld is None else ld
+    need = lib().gptq_prepare_plan(n, ld, r, None, 0)
     if need < 0:
         _check(int(need))
     buf = np.zeros((need, PLAN_FIELDS), dtype=np.int64)
-    got = lib().gptq_prepare_plan(n, ld, buf.ctypes.data_as(ctypes.POINTER(_i64)), need)
+    got = lib().gptq_prepare_plan(n, ld, r, buf.ctypes.data_as(ctypes.POINTER(_i64)), need)
     assert got == need
     return buf[0], buf[1:]
 

@@ -9,7 +9,10 @@
     time) never touch the same entries with one of them writing (accesses as rectangles,
     so the check is conservative); launches run in stream order;
   * the launch count and the placement of the work: one leaf per 128-block, every tree
-    product exactly once, each after the launches that complete its inputs.
+    product exactly once, each after the launches that complete its inputs;
+  * with the enclosing node's Q = P G22 carried along (the block as the left half of a
+    recursion node), Q comes out equal to P times the upper triangle of G22, its K chunks
+    in consecutive launches, and the rest as without it.
 """
 
 import numpy as np
@@ -27,8 +30,8 @@ def _gemm(rec):
     return dict(zip(names, (int(v) for v in rec)))
 
 
-def _ops(n):
-    head, ops = G.prepare_plan(n)
+def _ops(n, r=0):
+    head, ops = G.prepare_plan(n, r=r)
     out = []
     for r in ops:
         o = dict(kind=int(r[0]), off=int(r[3]), n=int(r[4]))
@@ -91,13 +94,19 @@ def _run_gemm(bufs, g):
             C[r0:r1, c0:c1] = new
 
 
-def _execute(A_upper, n):
-    head, ops = _ops(n)
+def _execute(A_upper, n, r=0, G22=None, P=None):
+    """Runs the schedule of the n-block in an (n + r)-square matrix; with r > 0, G22 (upper,
+    r x r) sits right below and right of the block and P (n x r) is buffer 3."""
+    head, ops = _ops(n, r)
     panel, qs = int(head[2]), int(head[3])
-    mat = np.full((n, n), np.nan)
+    ld = n + r
+    mat = np.full((ld, ld), np.nan)
     iu = np.triu_indices(n)
-    mat[iu] = A_upper[iu]
-    bufs = [mat, np.full(panel, np.nan), np.full(max(qs, 1), np.nan)]
+    mat[:n, :n][iu] = A_upper[iu]
+    if r:
+        mat[n:, n:][np.triu_indices(r)] = G22[np.triu_indices(r)]
+    bufs = [mat, np.full(panel, np.nan), np.full(max(qs, 1), np.nan),
+            P.copy() if r else np.full(1, np.nan), np.full((max(n * r, 1),), np.nan)]
     for o in ops:
         if o["n"] > 0:
             a, m = o["off"], o["n"]
@@ -108,7 +117,7 @@ def _execute(A_upper, n):
             blk[bi] = Gk[bi]
         for g in o["g"]:
             _run_gemm(bufs, g)
-    return mat, bufs[1].reshape(n, n)
+    return mat[:n, :n], bufs[1].reshape(n, n), bufs[4].reshape(n, r) if r else None
 
 
 def _spd(n, seed):
@@ -123,7 +132,7 @@ def _spd(n, seed):
 @pytest.mark.parametrize("n", [256, 1100, 2048])
 def test_schedule_computes_the_factor(n):
     Hd = _spd(n, 7 + n)
-    got, Us = _execute(Hd, n)
+    got, Us, _ = _execute(Hd, n)
     ref = O.inv_chol_upper(Hd)
     up = np.triu(got)
     assert np.all(np.isfinite(up))
@@ -138,15 +147,20 @@ def test_schedule_computes_the_factor(n):
         assert np.max(np.abs(Us[:c0, c0:c1] - U[:c0, c0:c1])) < 1e-9 * np.abs(U).max()
 
 
-def _parts(o, n):
+def _parts(o, n, ld=None, r=0):
     """Accesses of each part of one launch: [(buffer, row0, row1, col0, col1, writes)] for
     the leaf and for each product (its operands whole, its output tile by tile); buffer 2
     (the tree scratch) is addressed as one column."""
     parts = []
+    ld0 = n if ld is None else ld
 
     def rect(acc, b, off, rows, cols, ld, w, r_in=None):
         if b == 1:
             assert ld == n
+        if b == 0:
+            assert ld == ld0
+        if b in (3, 4):
+            assert ld == r
         if b == 2:
             lo = off + (r_in[0] * ld if r_in else 0)
             hi = off + ((r_in[1] - 1) * ld + cols if r_in else (rows - 1) * ld + cols)
@@ -157,7 +171,7 @@ def _parts(o, n):
 
     if o["n"] > 0:
         acc = []
-        rect(acc, 0, o["off"] * n + o["off"], o["n"], o["n"], n, True)
+        rect(acc, 0, o["off"] * ld0 + o["off"], o["n"], o["n"], ld0, True)
         parts.append(acc)
     for g in o["g"]:
         acc = []
@@ -177,12 +191,13 @@ def _overlap(a, b):
     return a[0] == b[0] and a[1] < b[2] and b[1] < a[2] and a[3] < b[4] and b[3] < a[4]
 
 
-@pytest.mark.parametrize("n", [1024, 1100, 2048, 4096])
-def test_launch_parts_are_disjoint(n):
-    head, ops = _ops(n)
+@pytest.mark.parametrize("n,r", [(1024, 0), (1100, 0), (2048, 0), (4096, 0), (1024, 1024),
+                                 (1536, 1600), (2048, 2048)])
+def test_launch_parts_are_disjoint(n, r):
+    head, ops = _ops(n, r)
     conflicts = 0
     for o in ops:
-        parts = _parts(o, n)
+        parts = _parts(o, n, n + r, r)
         for i in range(len(parts)):
             for j in range(i + 1, len(parts)):
                 for a in parts[i]:
@@ -221,8 +236,37 @@ def test_launch_structure(n):
         assert t1 == -(-g["M"] // 64) * -(-g["N"] // 64)
 
 
+@pytest.mark.parametrize("n,r", [(1024, 1024), (1100, 900)])
+def test_schedule_carries_the_node_q(n, r):
+    rng = np.random.default_rng(n + r)
+    Hd = _spd(n, 11 + n)
+    G22 = np.triu(rng.standard_normal((r, r))) + 4.0 * np.eye(r)
+    P = rng.standard_normal((n, r))
+    got, _, Q = _execute(Hd, n, r, G22, P)
+    ref = O.inv_chol_upper(Hd)
+    scale = np.abs(ref).max(axis=1, keepdims=True)
+    assert np.max(np.abs(np.triu(got) - ref) / scale) < 1e-9
+    Qr = P @ np.triu(G22)
+    assert np.max(np.abs(Q - Qr)) < 1e-9 * np.abs(Qr).max()
+    # the chunks: consecutive K ranges of at most 512, each in a later launch
+    head, ops = _ops(n, r)
+    assert int(head[1]) == r
+    where = [(i, g) for i, o in enumerate(ops) for g in o["g"] if g["Cb"] == 4]
+    k0s = sorted({g["Bo"] // (n + r) - n for _, g in where})
+    assert k0s == list(range(0, r, 512))
+    last = {}
+    for i, g in where:
+        k0 = g["Bo"] // (n + r) - n
+        assert g["beta"] == (0 if k0 == 0 else 1) and g["K"] == min(512, r - k0)
+        last[k0] = max(last.get(k0, -1), i)
+        if k0 > 0:
+            assert i > last[k0 - 512]
+
+
 def test_plan_rejects_bad_sizes():
     lib = G.lib()
-    assert lib.gptq_prepare_plan(0, 10, None, 0) == G.EINVAL
-    assert lib.gptq_prepare_plan(100, 99, None, 0) == G.EINVAL
-    assert lib.gptq_prepare_plan(128, 128, None, 0) == 2   # header and the single leaf
+    assert lib.gptq_prepare_plan(0, 10, 0, None, 0) == G.EINVAL
+    assert lib.gptq_prepare_plan(100, 99, 0, None, 0) == G.EINVAL
+    assert lib.gptq_prepare_plan(100, 150, 60, None, 0) == G.EINVAL   # ld < n + r
+    assert lib.gptq_prepare_plan(100, 100, -1, None, 0) == G.EINVAL
+    assert lib.gptq_prepare_plan(128, 128, 0, None, 0) == 2   # header and the single leaf
