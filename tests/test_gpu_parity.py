@@ -110,8 +110,9 @@ def _workload_h(d, n_tok, wid=93, outlier_frac=0.0):
 
 # d = 99 and 130 (not multiples of 4) take the element-wise copy and clear; the others the
 # 16-byte ones.  d = 1024, 1100 (a ragged last block) and 2048 take the blocked schedule,
-# the others the recursion.
-@pytest.mark.parametrize("d", [99, 100, 128, 130, 200, 320, 1024, 1100, 2048])
+# d = 3000 one recursion split (1408 + 1592) whose blocked left half also forms the split's
+# Q for a ragged right half, the others the recursion alone.
+@pytest.mark.parametrize("d", [99, 100, 128, 130, 200, 320, 1024, 1100, 2048, 3000])
 def test_prepare_against_oracle(d):
     torch = _torch()
     say("prepare", d)
