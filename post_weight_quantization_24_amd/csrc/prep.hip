@@ -461,7 +461,6 @@ __global__ void __launch_bounds__(256, 2) prep_fused(FusedArgs a) {
   }
 }
 
-
 // Blocks factored by the blocked schedule (prep_plan.h) instead of the recursion below.
 // Measured on MI355X (prepare at d = 1024 ... 11008): from 1024 it beats the recursion; up to
 // 2048 its trailing updates and tree products fit beside the leaves, while at 4096 the
