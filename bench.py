@@ -64,36 +64,19 @@ def parse():
     return p.parse_args()
 
 
-LEAF = 128   # block size below which the inverse factor is done by one workgroup
-
-
-def prep_gemm_flops(n):
-    """Useful flops of the products of the inverse-factor recursion on an n-block: for the
-    split n = m + r, P = A12 G22^T and Q = P G22 (m r (r+1) each, triangular G22), the
-    Schur update A11 -= P P^T (upper triangle, m (m+1) r) and G12 = -G11 Q (m (m+1) r)."""
-    if n <= LEAF:
-        return 0
-    m = (n // 2) // LEAF * LEAF or n - LEAF
-    r = n - m
-    return 2 * m * r * (r + 1) + 2 * m * (m + 1) * r + prep_gemm_flops(m) + prep_gemm_flops(r)
-
-
-def leaf_sizes(n):
-    if n <= LEAF:
-        return [n]
-    m = (n // 2) // LEAF * LEAF or n - LEAF
-    return leaf_sizes(m) + leaf_sizes(n - m)
+# Kernel families of the inverse factor.  Its blocked schedule runs trailing updates and tree
+# products inside the launches that carry a leaf, so the work is not split between these
+# families: they are timed one by one, and the roofline is taken for the phase as a whole.
+PREP_FAMILIES = ("prep_damp", "prep_leaf", "prep_gemm")
 
 
 def family_work(fam, d_row, d_col, n_tok, bits, block, x_dtype):
     """Algorithmic work of one step for a kernel family: (amount, unit, peak, bound)."""
     f32, f16, hbm = PEAK["mfma_f32"], PEAK["mfma_f16"], PEAK["hbm"]
+    if fam == "prepare":           # the factor H_d = U U^T and its inverse: d^3 / 3 flops each
+        return 2 * d_col ** 3 // 3, "TFLOP/s", f32, "mfma"
     if fam == "hessian_mfma":      # the d (d + 1) / 2 distinct entries, 2 flops per token each
         return n_tok * d_col * (d_col + 1), "TFLOP/s", f16 if x_dtype == "f16" else f32, "mfma"
-    if fam == "prep_gemm":
-        return prep_gemm_flops(d_col), "TFLOP/s", f32, "mfma"
-    if fam == "prep_leaf":         # factor and invert: n^3 / 3 flops each
-        return sum(2 * n ** 3 // 3 for n in leaf_sizes(d_col)), "TFLOP/s", f32, "mfma"
     if fam == "lazy_gemm":         # sum over blocks of 2 d_row B (d_col - j - B)
         return d_row * d_col * (d_col - block), "TFLOP/s", f32, "mfma"
     if fam == "quant_block":       # read W, write E and codes, read the G blocks
@@ -108,8 +91,8 @@ def family_work(fam, d_row, d_col, n_tok, bits, block, x_dtype):
 
 
 KERNEL_SOURCE = {   # kernel family -> the source file its counters were taken from
-    "hessian_mfma": "hessian.hip", "hessian_reduce": "hessian.hip", "prep_leaf": "prep.hip",
-    "prep_gemm": "gemm.hip", "lazy_gemm": "gemm.hip", "quant_block": "quant.hip",
+    "hessian_mfma": "hessian.hip", "hessian_reduce": "hessian.hip", "lazy_gemm": "gemm.hip",
+    "quant_block": "quant.hip",
 }
 
 
@@ -389,11 +372,19 @@ def configs_leg(G, torch, dev, reps=3):
                     for fam, (n, ms) in list(f_h.items()) + list(f_p.items()) + list(f_q.items()):
                         if not n:
                             continue
+                        if fam in PREP_FAMILIES:      # timed alone; the roofline is "prepare"'s
+                            phases[fam] = {"ms": ms, "launches": n}
+                            continue
                         work, unit, peak, bound = family_work(fam, d_row, d, n_tok, bits, block,
                                                               "f16")
                         ach = work / (ms / 1e3) / (1e12 if unit == "TFLOP/s" else 1e9)
                         phases[fam] = {"ms": ms, "launches": n, "bound": bound, "achieved": ach,
                                        "unit": unit, "frac": ach / peak}
+                    work, unit, peak, bound = family_work("prepare", d_row, d, n_tok, bits, block,
+                                                          "f16")
+                    ach = work / (t_p / 1e3) / 1e12   # t_p: the whole call, between HIP events
+                    phases["prepare"] = {"ms": t_p, "bound": bound, "achieved": ach, "unit": unit,
+                                         "frac": ach / peak}
                     t_layer = t_h / k + t_p / k + t_q
                     out.append({
                         "workload": wl_name, "layer": layer_name, "d_row": d_row, "d_col": d,
@@ -564,12 +555,23 @@ def main():
     torch.cuda.synchronize()
     G.profile_enable(False)
     phases = read_phases(1)
-    dom = max(phases, key=lambda k: phases[k]["ms_per_step"])
+    dom = max((f for f in phases if f not in PREP_FAMILIES), key=lambda k: phases[k]["ms_per_step"])
     for f, ph in phases.items():     # each family against its own roofline (this one step)
+        if f in PREP_FAMILIES:
+            continue
         work, unit, peak, bound = family_work(f, d_row, d_col, n_tok, bits, block, wl.dtype)
         ach = work / (ph["ms_per_step"] / 1e3) / (1e12 if unit == "TFLOP/s" else 1e9)
         ph.update({"bound": bound, "achieved": ach, "peak": peak, "unit": unit,
                    "frac": ach / peak})
+    prep = [phases[f] for f in PREP_FAMILIES if f in phases]
+    if prep:                         # the inverse factor as one phase (event overhead included)
+        work, unit, peak, bound = family_work("prepare", d_row, d_col, n_tok, bits, block,
+                                              wl.dtype)
+        ms_p = sum(ph["ms_per_step"] for ph in prep)
+        ach = work / (ms_p / 1e3) / 1e12
+        phases["prepare"] = {"launches_per_step": sum(ph["launches_per_step"] for ph in prep),
+                             "ms_per_step": ms_p, "bound": bound, "achieved": ach, "peak": peak,
+                             "unit": unit, "frac": ach / peak}
     quant_ms = sum(phases[f]["ms_per_step"] for f in
                    ("quant_convert", "quant_group_params", "quant_block", "lazy_gemm")
                    if f in phases)
